@@ -1,0 +1,40 @@
+"""fp64 CPU oracle for selected-block attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The GPU library never calls it and shares no code with
+it: the two meet only in the seeded input bytes from ``synth``.
+
+What it computes, step by step, in the order of the method:
+
+* ``keep_blocks``   - blocks kept per query-block row from a target sparsity;
+* ``pool``          - per-block means of Q and K over valid tokens;
+* ``block_scores``  - fp32 block scores (correctly rounded dot products);
+* ``select``        - per-query-head block indices and counts, protected
+                      prefix always kept, top-k with ties to the lower index;
+* ``attend``        - non-causal softmax attention over the selected blocks,
+                      padded keys excluded, GQA head h -> KV head h // G;
+* ``dense``         - the same with every block selected.
+
+Sources (web pages): vllm-omni PR #8335 "[Core] Add shared block-sparse
+attention adapters with FlashAttention-4" (Purpose: selector producing
+per-query-head block indices/counts, protected KV prefixes, suffix padding,
+native MHA/MQA/GQA mapping; 75 % target sparsity); diffusers
+``examples/cosmos3/cosmos_parallel.py`` (``_repeat_kv_heads``: query head i
+pairs with KV group i // repeats; ``build_gen_key_mask``: padded und and gen
+keys masked; ``cosmos3_cp_attention``: the generation pathway attends with full
+attention to cat(und, gen)); mstar PR #927 (automated review: default softmax
+scale head_dim**-0.5).
+
+Parity: every function here is pinned by CPU tests against closed forms,
+brute force, exact rational arithmetic and torch's fp64 SDPA; none is
+"parity unpinned".
+"""
+from .selector import keep_blocks, valid_key_mask, valid_query_mask, pool, block_scores, \
+    select, select_from_scores, rn32_exact, widen_bf16
+from .attention import attend, attend_rows, dense, identity_selection
+
+__all__ = [
+    "keep_blocks", "valid_key_mask", "valid_query_mask", "pool", "block_scores", "select",
+    "select_from_scores", "rn32_exact", "widen_bf16", "attend", "attend_rows", "dense",
+    "identity_selection",
+]
