@@ -1,0 +1,275 @@
+"""Python binding of libbsattn: selected-block attention on MI355X (gfx950).
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/bsattn.h``; PyTorch provides device
+memory and the stream. There is no fallback of any kind: if the library is
+missing, importing this package fails, and a failing call raises
+``BsAttnError`` with the library's own description (vllm-omni PR #8335,
+Purpose: provider failures propagate without dense fallback or K/V
+expansion).
+
+Tensors: q ``[B, q_len, Hq, D]``, k / v ``[B, kv_len, Hkv, D]``, bf16 on the
+GPU, last dimension contiguous. ``layout`` is a mapping with the integer
+fields of ``attn_shape`` (batch, num_q_heads, num_kv_heads, head_dim,
+block_q, block_k, q_len, q_valid, kv_prefix_len, kv_prefix_valid, kv_len,
+kv_suffix_valid) and optionally ``scale``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsattn.so")
+
+ATTN_OK = 0
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "LAUNCH", 5: "DEVICE"}
+
+
+class BsAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{STATUS_NAMES.get(status, status)}] {message}")
+        self.status = status
+
+
+class AttnShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("q_len", ctypes.c_int32), ("q_valid", ctypes.c_int32),
+        ("kv_prefix_len", ctypes.c_int32), ("kv_prefix_valid", ctypes.c_int32),
+        ("kv_len", ctypes.c_int32), ("kv_suffix_valid", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+EXPORTS = ("attn_keep_blocks", "attn_select_workspace_size", "attn_select_blocks",
+           "attn_block_sparse_fwd", "attn_dense_fwd", "attn_query_support",
+           "attn_last_error", "attn_version")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+            "g.build()' or python block_sparse_attention_blocks_amd/build.py)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    SH = ctypes.POINTER(AttnShape)
+    lib.attn_keep_blocks.argtypes = [I32, I32, I32]
+    lib.attn_keep_blocks.restype = I32
+    lib.attn_select_workspace_size.argtypes = [SH]
+    lib.attn_select_workspace_size.restype = SZ
+    lib.attn_select_blocks.argtypes = [SH, P, P, I32, P, P, I32, P, SZ, P]
+    lib.attn_select_blocks.restype = I32
+    lib.attn_block_sparse_fwd.argtypes = [SH, P, P, P, P, P, I32, P, P, P]
+    lib.attn_block_sparse_fwd.restype = I32
+    lib.attn_dense_fwd.argtypes = [SH, P, P, P, P, P, P]
+    lib.attn_dense_fwd.restype = I32
+    lib.attn_query_support.argtypes = [SH]
+    lib.attn_query_support.restype = I32
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    return lib
+
+
+lib = _load()
+
+
+def version() -> str:
+    return lib.attn_version().decode()
+
+
+def last_error() -> str:
+    return lib.attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise BsAttnError(status, last_error())
+
+
+_FIELDS = ("batch", "num_q_heads", "num_kv_heads", "head_dim", "block_q", "block_k", "q_len",
+           "q_valid", "kv_prefix_len", "kv_prefix_valid", "kv_len", "kv_suffix_valid")
+
+
+def make_shape(layout, q=None, k=None, v=None, out=None) -> AttnShape:
+    """attn_shape from a layout mapping; strides from the tensors given
+    (contiguous [B, L, H, D] strides where a tensor is not given)."""
+    s = AttnShape()
+    for f in _FIELDS:
+        setattr(s, f, int(layout[f]))
+    d = int(layout["head_dim"])
+    hq, hkv = int(layout["num_q_heads"]), int(layout["num_kv_heads"])
+
+    def strides(t, length, heads):
+        if t is not None:
+            if t.stride(-1) != 1:
+                raise ValueError("the last (head_dim) dimension must be contiguous")
+            return t.stride(0), t.stride(1), t.stride(2)
+        return length * heads * d, heads * d, d
+
+    s.q_stride[:] = strides(q, int(layout["q_len"]), hq)
+    s.k_stride[:] = strides(k, int(layout["kv_len"]), hkv)
+    s.v_stride[:] = strides(v, int(layout["kv_len"]), hkv)
+    s.o_stride[:] = strides(out, int(layout["q_len"]), hq)
+    scale = layout.get("scale") if hasattr(layout, "get") else None
+    s.softmax_scale = float(scale) if scale is not None else 0.0
+    return s
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _check_tensor(t, name, dtype, device=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def keep_blocks(n_kv_blocks: int, n_protected: int, sparsity_pct: int) -> int:
+    """Kept blocks per row for a target sparsity (protected blocks included)."""
+    k = lib.attn_keep_blocks(n_kv_blocks, n_protected, sparsity_pct)
+    if k < 0:
+        raise ValueError("need 0 <= n_protected <= n_kv_blocks and 0 <= sparsity_pct <= 100")
+    return k
+
+
+def num_blocks(layout):
+    """(NQ, NK, P) of a layout."""
+    return (int(layout["q_len"]) // int(layout["block_q"]),
+            int(layout["kv_len"]) // int(layout["block_k"]),
+            int(layout["kv_prefix_len"]) // int(layout["block_k"]))
+
+
+def select_workspace_size(layout) -> int:
+    n = lib.attn_select_workspace_size(ctypes.byref(make_shape(layout)))
+    if n == 0:
+        _check(lib.attn_query_support(ctypes.byref(make_shape(layout))))
+    return n
+
+
+def select_blocks(q, k, layout, keep: int, idx_row_stride=None, *, block_idx=None,
+                  block_cnt=None, workspace=None, stream=None):
+    """Per-query-head KV-block indices and counts (attn_select_blocks).
+    Returns (block_idx [B,Hq,NQ,stride] int32, block_cnt [B,Hq,NQ] int32)."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16)
+    _check_tensor(k, "k", torch.bfloat16, q.device)
+    shape = make_shape(layout, q=q, k=k)
+    nq, nk, _ = num_blocks(layout)
+    stride = int(keep if idx_row_stride is None else idx_row_stride)
+    stride = max(stride, 1)
+    b, hq = int(layout["batch"]), int(layout["num_q_heads"])
+    if block_idx is None:
+        block_idx = torch.empty((b, hq, nq, stride), dtype=torch.int32, device=q.device)
+    if block_cnt is None:
+        block_cnt = torch.empty((b, hq, nq), dtype=torch.int32, device=q.device)
+    ws_bytes = lib.attn_select_workspace_size(ctypes.byref(shape))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_select_blocks(ctypes.byref(shape), _ptr(q), _ptr(k), int(keep),
+                                  _ptr(block_idx), _ptr(block_cnt), stride, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream)))
+    return block_idx, block_cnt
+
+
+def block_sparse_attention(q, k, v, block_idx, block_cnt, layout, *, out=None, return_lse=False,
+                           stream=None):
+    """Attention over the selected blocks (attn_block_sparse_fwd)."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16)
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, torch.bfloat16, q.device)
+    _check_tensor(block_idx, "block_idx", torch.int32, q.device)
+    _check_tensor(block_cnt, "block_cnt", torch.int32, q.device)
+    if not (block_idx.is_contiguous() and block_cnt.is_contiguous()):
+        raise ValueError("block_idx and block_cnt must be contiguous")
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = None
+    if return_lse:
+        lse = torch.empty((int(layout["batch"]), int(layout["num_q_heads"]), int(layout["q_len"])),
+                          dtype=torch.float32, device=q.device)
+    shape = make_shape(layout, q=q, k=k, v=v, out=out)
+    _check(lib.attn_block_sparse_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(block_idx), _ptr(block_cnt), int(block_idx.shape[-1]),
+                                     _ptr(out), _ptr(lse), _stream_handle(stream)))
+    return (out, lse) if return_lse else out
+
+
+def dense_attention(q, k, v, layout, *, out=None, return_lse=False, stream=None):
+    """Dense attention through the same kernel (attn_dense_fwd)."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16)
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, torch.bfloat16, q.device)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = None
+    if return_lse:
+        lse = torch.empty((int(layout["batch"]), int(layout["num_q_heads"]), int(layout["q_len"])),
+                          dtype=torch.float32, device=q.device)
+    shape = make_shape(layout, q=q, k=k, v=v, out=out)
+    _check(lib.attn_dense_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                              _ptr(lse), _stream_handle(stream)))
+    return (out, lse) if return_lse else out
+
+
+def query_support(layout):
+    """(status, message) of attn_query_support for a layout."""
+    st = lib.attn_query_support(ctypes.byref(make_shape(layout)))
+    return st, (last_error() if st else "")
+
+
+def pad_segments(q_gen, k_prefix, v_prefix, k_gen, v_gen, block_q: int, block_k: int, scale=None):
+    """Request preparation (vllm-omni PR #8335, Purpose: the shared layer owns
+    protected prefixes and suffix padding): pad the query stream to block_q and
+    each key/value segment to block_k on its own (diffusers cosmos_parallel.py,
+    shard_cosmos3_sequence), and return (q, k, v, layout). Inputs are
+    [B, L, H, D] bf16 GPU tensors; k_prefix/v_prefix may have length 0."""
+    import torch
+    b, lg, hq, d = q_gen.shape
+    lp, hkv = k_prefix.shape[1], k_prefix.shape[2]
+
+    def up(n, m):
+        return ((n + m - 1) // m) * m
+
+    ql, pl, gl = up(lg, block_q), up(lp, block_k), up(k_gen.shape[1], block_k)
+    q = torch.zeros((b, ql, hq, d), dtype=q_gen.dtype, device=q_gen.device)
+    q[:, :lg] = q_gen
+    k = torch.zeros((b, pl + gl, hkv, d), dtype=k_gen.dtype, device=k_gen.device)
+    v = torch.zeros_like(k)
+    k[:, :lp] = k_prefix
+    v[:, :lp] = v_prefix
+    k[:, pl:pl + k_gen.shape[1]] = k_gen
+    v[:, pl:pl + v_gen.shape[1]] = v_gen
+    layout = dict(batch=b, num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_q=block_q,
+                  block_k=block_k, q_len=ql, q_valid=lg, kv_prefix_len=pl, kv_prefix_valid=lp,
+                  kv_len=pl + gl, kv_suffix_valid=k_gen.shape[1], scale=scale)
+    return q, k, v, layout
+
+
+__all__ = ["BsAttnError", "AttnShape", "EXPORTS", "LIB_PATH", "lib", "version", "last_error",
+           "make_shape", "keep_blocks", "num_blocks", "select_workspace_size", "select_blocks",
+           "block_sparse_attention", "dense_attention", "query_support", "pad_segments"]

@@ -1,0 +1,359 @@
+// Host side of libbsattn: argument validation, workspace layout, launches,
+// error reporting. The C ABI is declared in include/bsattn.h.
+//
+// Contract points taken from the pages: the selector produces per-query-head
+// block indices and counts and the backend executes them; failures
+// propagate with no dense fallback and no K/V expansion; sparse capability is
+// checked on its own (vllm-omni PR #8335 "[Core] Add shared block-sparse
+// attention adapters with FlashAttention-4", Purpose). A failure names what
+// failed, the library version and the target (in the spirit of the startup
+// check of mstar PR #927, "Since the review").
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "bsattn.h"
+#include "internal.h"
+
+#define BSATTN_VERSION "0.1.0"
+#define BSATTN_TARGET "gfx950"
+
+namespace {
+
+thread_local std::string t_last_error;
+
+attn_status fail(attn_status st, const char* fn, const char* fmt, ...) {
+  char msg[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  char full[768];
+  snprintf(full, sizeof full, "%s: %s [libbsattn %s, %s]", fn, msg, BSATTN_VERSION, BSATTN_TARGET);
+  t_last_error = full;
+  return st;
+}
+
+attn_status ok() {
+  t_last_error.clear();
+  return ATTN_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Everything about the shape that the kernels rely on.
+attn_status validate_shape(const attn_shape* s, const char* fn) {
+  if (s == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "shape is NULL");
+  if (s->batch < 1) return fail(ATTN_ERR_INVALID_ARG, fn, "batch %d < 1", s->batch);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "head counts must be >= 1 (Hq %d, Hkv %d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "head_dim %d unsupported (supported: 64, 128)",
+                s->head_dim);
+  if ((s->block_q != 64 && s->block_q != 128) || (s->block_k != 64 && s->block_k != 128))
+    return fail(ATTN_ERR_UNSUPPORTED, fn,
+                "block geometry %dx%d unsupported (block_q and block_k in {64, 128})", s->block_q,
+                s->block_k);
+  if (s->q_len < 0 || s->q_len % s->block_q != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "q_len %d is not a non-negative multiple of block_q %d",
+                s->q_len, s->block_q);
+  if (s->q_valid < 0 || s->q_valid > s->q_len)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "q_valid %d outside [0, q_len %d]", s->q_valid, s->q_len);
+  if (s->kv_prefix_len < 0 || s->kv_prefix_len % s->block_k != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn,
+                "kv_prefix_len %d is not a non-negative multiple of block_k %d", s->kv_prefix_len,
+                s->block_k);
+  if (s->kv_prefix_valid < 0 || s->kv_prefix_valid > s->kv_prefix_len)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "kv_prefix_valid %d outside [0, kv_prefix_len %d]",
+                s->kv_prefix_valid, s->kv_prefix_len);
+  if (s->kv_len < s->kv_prefix_len || s->kv_len % s->block_k != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn,
+                "kv_len %d must be a multiple of block_k %d and >= kv_prefix_len %d", s->kv_len,
+                s->block_k, s->kv_prefix_len);
+  if (s->kv_suffix_valid < 0 || s->kv_suffix_valid > s->kv_len - s->kv_prefix_len)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "kv_suffix_valid %d outside [0, kv_len - kv_prefix_len = %d]",
+                s->kv_suffix_valid, s->kv_len - s->kv_prefix_len);
+  const int64_t* strides[4] = {s->q_stride, s->k_stride, s->v_stride, s->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int a = 0; a < 4; ++a)
+    for (int d = 0; d < 3; ++d)
+      if (strides[a][d] < 0 || strides[a][d] % 8 != 0)
+        return fail(ATTN_ERR_UNSUPPORTED, fn,
+                    "%s_stride[%d] = %lld must be a non-negative multiple of 8 elements", names[a],
+                    d, (long long)strides[a][d]);
+  if (!(std::isfinite(s->softmax_scale)))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "softmax_scale is not finite");
+  if (s->batch > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "batch %d > 65535", s->batch);
+  const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / s->block_q);
+  if (nwg > 0x7FFFFFFF) return fail(ATTN_ERR_UNSUPPORTED, fn, "grid too large");
+  return ATTN_OK;
+}
+
+attn_status validate_ptr(const char* fn, const char* name, const void* ptr) {
+  if (ptr == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "%s is NULL", name);
+  if (!aligned16(ptr)) return fail(ATTN_ERR_UNSUPPORTED, fn, "%s is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+attn_status validate_tensors(const char* fn, const void* q, const void* k, const void* v,
+                             const void* o, const float* lse) {
+  attn_status st;
+  if ((st = validate_ptr(fn, "q", q)) != ATTN_OK) return st;
+  if ((st = validate_ptr(fn, "k", k)) != ATTN_OK) return st;
+  if ((st = validate_ptr(fn, "v", v)) != ATTN_OK) return st;
+  if ((st = validate_ptr(fn, "out", o)) != ATTN_OK) return st;
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "lse is not 4-byte aligned");
+  return ATTN_OK;
+}
+
+// The current device must be a gfx950; the answer is cached per device.
+attn_status check_device(const char* fn) {
+  static std::atomic<int> state[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(ATTN_ERR_DEVICE, fn, "no HIP device available");
+  if (dev >= 64) return fail(ATTN_ERR_DEVICE, fn, "device ordinal %d too large", dev);
+  int st = state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(ATTN_ERR_DEVICE, fn, "cannot query device %d", dev);
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    state[dev].store(st, std::memory_order_relaxed);
+    if (st < 0)
+      return fail(ATTN_ERR_DEVICE, fn, "device %d is %s, this library runs on gfx950 only", dev,
+                  prop.gcnArchName);
+  }
+  if (st < 0) return fail(ATTN_ERR_DEVICE, fn, "device %d is not a gfx950", dev);
+  return ATTN_OK;
+}
+
+struct Derived {
+  int nq, nk, P, n_forced, n_cand, group;
+};
+
+Derived derive(const attn_shape* s) {
+  Derived d;
+  d.nq = s->q_len / s->block_q;
+  d.nk = s->kv_len / s->block_k;
+  d.P = s->kv_prefix_len / s->block_k;
+  d.n_forced = (int)ceil_div(s->kv_prefix_valid, s->block_k);
+  d.n_cand = (int)ceil_div(s->kv_suffix_valid, s->block_k);
+  d.group = s->num_q_heads / s->num_kv_heads;
+  return d;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t qp, qn, kpt, kn, total;
+};
+
+WsLayout ws_layout(const attn_shape* s) {
+  const Derived d = derive(s);
+  const size_t B = (size_t)s->batch, D = (size_t)s->head_dim;
+  WsLayout w;
+  w.qp = 0;
+  w.qn = w.qp + round256(B * s->num_q_heads * d.nq * D * sizeof(double));
+  w.kpt = w.qn + round256(B * s->num_q_heads * d.nq * sizeof(double));
+  w.kn = w.kpt + round256(B * s->num_kv_heads * D * d.nk * sizeof(float));
+  w.total = w.kn + round256(B * s->num_kv_heads * d.nk * sizeof(double));
+  return w;
+}
+
+float scale_of(const attn_shape* s) {
+  return s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
+}
+
+attn_status run_attention(const char* fn, const attn_shape* s, const void* q, const void* k,
+                          const void* v, const int32_t* idx, const int32_t* cnt,
+                          int32_t idx_row_stride, void* out, float* lse, bool dense,
+                          hipStream_t stream) {
+  attn_status st = validate_shape(s, fn);
+  if (st != ATTN_OK) return st;
+  st = validate_tensors(fn, q, k, v, out, lse);
+  if (st != ATTN_OK) return st;
+  if (!dense) {
+    if (idx == nullptr || cnt == nullptr)
+      return fail(ATTN_ERR_INVALID_ARG, fn, "block_idx / block_cnt is NULL");
+    if ((reinterpret_cast<uintptr_t>(idx) & 3u) || (reinterpret_cast<uintptr_t>(cnt) & 3u))
+      return fail(ATTN_ERR_INVALID_ARG, fn, "block_idx / block_cnt not 4-byte aligned");
+    if (idx_row_stride < 1)
+      return fail(ATTN_ERR_INVALID_ARG, fn, "idx_row_stride %d < 1", idx_row_stride);
+  }
+  const Derived d = derive(s);
+  bsattn::AttnParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.idx = idx;
+  p.cnt = cnt;
+  p.qs0 = s->q_stride[0]; p.qs1 = s->q_stride[1]; p.qs2 = s->q_stride[2];
+  p.ks0 = s->k_stride[0]; p.ks1 = s->k_stride[1]; p.ks2 = s->k_stride[2];
+  p.vs0 = s->v_stride[0]; p.vs1 = s->v_stride[1]; p.vs2 = s->v_stride[2];
+  p.os0 = s->o_stride[0]; p.os1 = s->o_stride[1]; p.os2 = s->o_stride[2];
+  p.batch = s->batch;
+  p.hq = s->num_q_heads;
+  p.hkv = s->num_kv_heads;
+  p.group = d.group;
+  p.q_len = s->q_len;
+  p.q_valid = s->q_valid;
+  p.kv_prefix_len = s->kv_prefix_len;
+  p.kv_prefix_valid = s->kv_prefix_valid;
+  p.kv_suffix_valid = s->kv_suffix_valid;
+  p.nq = d.nq;
+  p.nk = d.nk;
+  p.n_prefix_blocks = d.P;
+  p.n_forced = d.n_forced;
+  p.n_cand = d.n_cand;
+  p.idx_row_stride = dense ? 0 : idx_row_stride;
+  p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq);
+  p.scale_log2 = scale_of(s) * 1.4426950408889634f;
+  if (p.n_wg == 0) return ok();
+  st = check_device(fn);
+  if (st != ATTN_OK) return st;
+  const hipError_t e = bsattn::launch_attention(p, s->head_dim, s->block_q, s->block_k, dense, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t attn_keep_blocks(int32_t n_kv_blocks, int32_t n_protected, int32_t sparsity_pct) {
+  if (n_kv_blocks < 0 || n_protected < 0 || n_protected > n_kv_blocks || sparsity_pct < 0 ||
+      sparsity_pct > 100)
+    return -1;
+  const int64_t k = ceil_div((int64_t)n_kv_blocks * (100 - sparsity_pct), 100);
+  int64_t r = k < n_protected ? n_protected : k;
+  if (r > n_kv_blocks) r = n_kv_blocks;
+  return (int32_t)r;
+}
+
+size_t attn_select_workspace_size(const attn_shape* shape) {
+  if (validate_shape(shape, "attn_select_workspace_size") != ATTN_OK) return 0;
+  return ws_layout(shape).total;
+}
+
+attn_status attn_select_blocks(const attn_shape* s, const void* q, const void* k,
+                               int32_t keep_blocks, int32_t* block_idx, int32_t* block_cnt,
+                               int32_t idx_row_stride, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  const char* fn = "attn_select_blocks";
+  attn_status st = validate_shape(s, fn);
+  if (st != ATTN_OK) return st;
+  if ((st = validate_ptr(fn, "q", q)) != ATTN_OK) return st;
+  if ((st = validate_ptr(fn, "k", k)) != ATTN_OK) return st;
+  const Derived d = derive(s);
+  if (keep_blocks < d.P || keep_blocks > d.nk)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "keep_blocks %d outside [P = %d, NK = %d]", keep_blocks,
+                d.P, d.nk);
+  if (idx_row_stride < keep_blocks || idx_row_stride < 1)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "idx_row_stride %d < max(keep_blocks %d, 1)",
+                idx_row_stride, keep_blocks);
+  if (block_idx == nullptr || block_cnt == nullptr)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "block_idx / block_cnt is NULL");
+  if ((reinterpret_cast<uintptr_t>(block_idx) & 3u) || (reinterpret_cast<uintptr_t>(block_cnt) & 3u))
+    return fail(ATTN_ERR_INVALID_ARG, fn, "block_idx / block_cnt not 4-byte aligned");
+  if (d.nk > 4096)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "%d KV blocks > 4096 supported by the selector", d.nk);
+  const WsLayout w = ws_layout(s);
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(ATTN_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu required", workspace_bytes,
+                w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(ATTN_ERR_WORKSPACE, fn, "workspace is not 256-byte aligned");
+  if (d.nq == 0) return ok();
+  st = check_device(fn);
+  if (st != ATTN_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+
+  bsattn::PoolParams pp{};
+  pp.q = static_cast<const uint16_t*>(q);
+  pp.k = static_cast<const uint16_t*>(k);
+  pp.qs0 = s->q_stride[0]; pp.qs1 = s->q_stride[1]; pp.qs2 = s->q_stride[2];
+  pp.ks0 = s->k_stride[0]; pp.ks1 = s->k_stride[1]; pp.ks2 = s->k_stride[2];
+  pp.hq = s->num_q_heads;
+  pp.hkv = s->num_kv_heads;
+  pp.bq = s->block_q;
+  pp.bk = s->block_k;
+  pp.q_valid = s->q_valid;
+  pp.kv_prefix_len = s->kv_prefix_len;
+  pp.kv_prefix_valid = s->kv_prefix_valid;
+  pp.kv_suffix_valid = s->kv_suffix_valid;
+  pp.nq = d.nq;
+  pp.nk = d.nk;
+  pp.qp = reinterpret_cast<double*>(ws + w.qp);
+  pp.qn = reinterpret_cast<double*>(ws + w.qn);
+  pp.kpt = reinterpret_cast<float*>(ws + w.kpt);
+  pp.kn = reinterpret_cast<double*>(ws + w.kn);
+  hipError_t e = bsattn::launch_pool(pp, s->head_dim, s->batch, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "pool launch failed: %s", hipGetErrorString(e));
+
+  bsattn::ScoreParams sp{};
+  sp.qp = pp.qp;
+  sp.qn = pp.qn;
+  sp.kpt = pp.kpt;
+  sp.kn = pp.kn;
+  sp.idx = block_idx;
+  sp.cnt = block_cnt;
+  sp.hq = s->num_q_heads;
+  sp.hkv = s->num_kv_heads;
+  sp.group = d.group;
+  sp.nq = d.nq;
+  sp.nk = d.nk;
+  sp.bq = s->block_q;
+  sp.q_valid = s->q_valid;
+  sp.n_prefix_blocks = d.P;
+  sp.n_forced = d.n_forced;
+  sp.n_cand = d.n_cand;
+  sp.keep = keep_blocks;
+  sp.idx_row_stride = idx_row_stride;
+  e = bsattn::launch_score_topk(sp, s->head_dim, s->batch, stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "score launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+attn_status attn_block_sparse_fwd(const attn_shape* s, const void* q, const void* k, const void* v,
+                                  const int32_t* block_idx, const int32_t* block_cnt,
+                                  int32_t idx_row_stride, void* out, float* lse,
+                                  hipStream_t stream) {
+  return run_attention("attn_block_sparse_fwd", s, q, k, v, block_idx, block_cnt, idx_row_stride,
+                       out, lse, false, stream);
+}
+
+attn_status attn_dense_fwd(const attn_shape* s, const void* q, const void* k, const void* v,
+                           void* out, float* lse, hipStream_t stream) {
+  return run_attention("attn_dense_fwd", s, q, k, v, nullptr, nullptr, 0, out, lse, true, stream);
+}
+
+attn_status attn_query_support(const attn_shape* s) {
+  const char* fn = "attn_query_support";
+  const attn_status st = validate_shape(s, fn);
+  if (st != ATTN_OK) return st;
+  if (derive(s).nk > 4096)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "%d KV blocks > 4096 supported by the selector",
+                derive(s).nk);
+  return ok();
+}
+
+const char* attn_last_error(void) { return t_last_error.c_str(); }
+
+const char* attn_version(void) { return BSATTN_VERSION; }
+
+}  // extern "C"

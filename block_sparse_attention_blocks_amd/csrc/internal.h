@@ -1,0 +1,65 @@
+// Internal declarations shared by the host entry points and the kernels of
+// libbsattn. Not part of the public ABI (that is include/bsattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+// Kernel-side description of one attention call (all sizes validated on the
+// host before any launch).
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;            // may be null
+  const int32_t* idx;    // sparse only
+  const int32_t* cnt;    // sparse only
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+  int32_t batch, hq, hkv, group;
+  int32_t q_len, q_valid, kv_prefix_len, kv_prefix_valid, kv_suffix_valid;
+  int32_t nq, nk;
+  int32_t n_prefix_blocks;  // P
+  int32_t n_forced;         // protected blocks holding a real key: [0, n_forced)
+  int32_t n_cand;           // generation blocks holding a real key: [P, P + n_cand)
+  int32_t idx_row_stride;
+  int32_t n_wg;             // workgroups in the grid
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+struct PoolParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+  int32_t hq, hkv, bq, bk, q_valid, kv_prefix_len, kv_prefix_valid, kv_suffix_valid;
+  int32_t nq, nk;
+  double* qp;    // [B][Hq][NQ][D]  pooled queries (fp32 values held exactly in fp64)
+  double* qn;    // [B][Hq][NQ]     upper bound of the L2 norm of each pooled query
+  float* kpt;    // [B][Hkv][D][NK] pooled keys, transposed
+  double* kn;    // [B][Hkv][NK]    upper bound of the L2 norm of each pooled key
+};
+
+struct ScoreParams {
+  const double* qp;
+  const double* qn;
+  const float* kpt;
+  const double* kn;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t hq, hkv, group, nq, nk, bq, q_valid;
+  int32_t n_prefix_blocks, n_forced, n_cand, keep, idx_row_stride;
+};
+
+// Launchers (return the HIP error of the launch).
+hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, bool dense,
+                            hipStream_t stream);
+hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t stream);
+hipError_t launch_score_topk(const ScoreParams& p, int head_dim, int batch, hipStream_t stream);
+
+// Rows of the score kernel per workgroup and its dynamic LDS bytes.
+int score_rows_per_wg(int n_cand);
+size_t score_lds_bytes(int n_cand);
+
+}  // namespace bsattn

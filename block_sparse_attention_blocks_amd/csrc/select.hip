@@ -1,0 +1,363 @@
+// Block selector kernels for gfx950: block-mean pooling of Q and K, then
+// per-row block scores and a deterministic top-k.
+//
+// The selector's contract is that of vllm-omni PR #8335 "[Core] Add shared
+// block-sparse attention adapters with FlashAttention-4" (Purpose): it
+// produces per-query-head KV-block indices and counts, always keeps the
+// protected KV prefix, and query head h works against KV head h / G (native
+// GQA mapping, no K/V expansion). The pages leave the scoring rule open; the
+// reading implemented here is block-mean pooling of Q and K with the fp32 dot
+// product of the pooled vectors as the block score, top-k by (score
+// descending, index ascending).
+//
+// Exactness: the pooled vectors are the exact block sums (fp64 sums of bf16
+// values) divided once in fp64 and rounded once to fp32; each score is the
+// fp32 value nearest to the exact dot product of two pooled vectors. The fast
+// path is an fp64 dot product with a rigorous error bound; when that bound
+// leaves the fp32 rounding open, the score is recomputed with an exact
+// 576-bit fixed-point accumulator. The selected set is therefore a pure
+// function of the input bytes.
+
+#include "internal.h"
+
+namespace bsattn {
+namespace {
+
+// ---------------------------------------------------------------- pooling
+// One workgroup per (batch, block) covers every head of that block: the
+// block's rows are contiguous [rows][heads][D] bf16, so the reads stream.
+template <int D>
+__global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
+  constexpr int CPH = D / 8;  // 16-byte chunks per head row
+  const int blk = blockIdx.x;
+  const int b = blockIdx.y;
+  const bool isq = blk < p.nq;
+  const int j = isq ? blk : blk - p.nq;
+  const int heads = isq ? p.hq : p.hkv;
+  const int bs = isq ? p.bq : p.bk;
+  const int start = j * bs;
+  int end;
+  if (isq) {
+    end = min(start + bs, p.q_valid);
+  } else {
+    const int seg_end =
+        (start < p.kv_prefix_len) ? p.kv_prefix_valid : p.kv_prefix_len + p.kv_suffix_valid;
+    end = min(start + bs, seg_end);
+  }
+  const int n = max(end - start, 0);
+  const uint16_t* base = isq ? p.q + (int64_t)b * p.qs0 : p.k + (int64_t)b * p.ks0;
+  const int64_t s1 = isq ? p.qs1 : p.ks1;
+  const int64_t s2 = isq ? p.qs2 : p.ks2;
+  const int nchunks = heads * CPH;
+  const int nblocks = isq ? p.nq : p.nk;
+
+  for (int c0 = 0; c0 < nchunks; c0 += 256) {
+    const int c = c0 + (int)threadIdx.x;
+    const bool act = c < nchunks;
+    const int hh = act ? c / CPH : 0;
+    const int dc = c % CPH;
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    if (act && n > 0) {
+      const uint16_t* src = base + (int64_t)start * s1 + (int64_t)hh * s2 + dc * 8;
+#pragma unroll 4
+      for (int t = 0; t < n; ++t) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)t * s1);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+          acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
+        }
+      }
+    }
+    float m32[8];
+    double sq = 0.0;
+    const double dn = (double)max(n, 1);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      m32[e] = n > 0 ? (float)(acc[e] / dn) : 0.0f;  // one fp64 division, one fp32 rounding
+      sq = __builtin_fma((double)m32[e], (double)m32[e], sq);
+    }
+#pragma unroll
+    for (int off = 1; off < CPH; off <<= 1) sq += __shfl_xor(sq, off);
+    if (act) {
+      if (isq) {
+        double* dst = p.qp + (((int64_t)b * p.hq + hh) * p.nq + j) * D + dc * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = (double)m32[e];
+      } else {
+        float* dst = p.kpt + (((int64_t)b * p.hkv + hh) * D + dc * 8) * p.nk + j;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[(int64_t)e * p.nk] = m32[e];
+      }
+      if (dc == 0) {
+        // Upper bound of the Euclidean norm (covers the rounding of sq and sqrt).
+        const double nrm = __builtin_sqrt(sq) * (1.0 + 0x1p-40);
+        (isq ? p.qn : p.kn)[((int64_t)b * heads + hh) * nblocks + j] = nrm;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- exact dot product
+// Exact sum of D products of fp32 pairs in a 576-bit two's complement fixed
+// point accumulator (bit 0 weighs 2^-298, below the smallest product
+// 2^-149 * 2^-149), then rounded to the nearest fp32, ties to even.
+// a: D values (fp32 held exactly in fp64), b: D fp32 values at stride bstride.
+__device__ __noinline__ float exact_dot_rn32(const double* a, const float* b, int64_t bstride,
+                                             int D) {
+  constexpr int NL = 9;
+  uint64_t acc[NL];
+#pragma unroll
+  for (int L = 0; L < NL; ++L) acc[L] = 0;
+  for (int d = 0; d < D; ++d) {
+    const uint32_t ua = __float_as_uint((float)a[d]);
+    const uint32_t ub = __float_as_uint(b[(int64_t)d * bstride]);
+    const uint32_t ea = (ua >> 23) & 0xFFu, eb = (ub >> 23) & 0xFFu;
+    const uint64_t ma = (ua & 0x7FFFFFu) | (ea ? 0x800000u : 0u);
+    const uint64_t mb = (ub & 0x7FFFFFu) | (eb ? 0x800000u : 0u);
+    const uint64_t m = ma * mb;  // < 2^48
+    if (m == 0) continue;
+    const int xa = ea ? (int)ea - 150 : -149;
+    const int xb = eb ? (int)eb - 150 : -149;
+    const int pos = xa + xb + 298;  // in [0, 506]
+    const int limb = pos >> 6, off = pos & 63;
+    const uint64_t lo = m << off;
+    const uint64_t hi = off ? (m >> (64 - off)) : 0;
+    const bool neg = ((ua ^ ub) >> 31) != 0;
+    // acc += (neg ? -X : X), X = lo * 2^(64 limb) + hi * 2^(64 (limb + 1)); -X = ~X + 1.
+    uint64_t carry = neg ? 1 : 0;
+#pragma unroll
+    for (int L = 0; L < NL; ++L) {
+      uint64_t x = (L == limb) ? lo : ((L == limb + 1) ? hi : 0);
+      if (neg) x = ~x;
+      const uint64_t s1 = acc[L] + x;
+      const uint64_t c1 = s1 < x;
+      const uint64_t s2 = s1 + carry;
+      const uint64_t c2 = s2 < carry;
+      acc[L] = s2;
+      carry = c1 | c2;
+    }
+  }
+  const bool negr = (acc[NL - 1] >> 63) != 0;
+  if (negr) {  // magnitude
+    uint64_t carry = 1;
+#pragma unroll
+    for (int L = 0; L < NL; ++L) {
+      const uint64_t x = ~acc[L];
+      const uint64_t s = x + carry;
+      carry = s < carry;
+      acc[L] = s;
+    }
+  }
+  int top = -1;  // highest set bit
+#pragma unroll
+  for (int L = NL - 1; L >= 0; --L)
+    if (top < 0 && acc[L] != 0) top = 64 * L + 63 - __clzll(acc[L]);
+  if (top < 0) return 0.0f;  // exact zero: +0
+  const int etop = top - 298;
+  if (etop >= 128) return negr ? -__builtin_inff() : __builtin_inff();
+  const int lsb = (etop >= -126) ? top - 23 : 149;  // weight 2^(lsb-298) of the last kept bit
+  const int sbit = lsb - 1;                          // round bit, >= 148
+  const int wl = sbit >> 6, wo = sbit & 63;
+  uint64_t w0 = 0, w1 = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int L = 0; L < NL; ++L) {
+    if (L == wl) {
+      w0 = acc[L];
+      sticky = sticky || (wo ? (acc[L] & ((1ull << wo) - 1)) != 0 : false);
+    }
+    if (L == wl + 1) w1 = acc[L];
+    if (L < wl) sticky = sticky || acc[L] != 0;
+  }
+  const uint64_t win = (w0 >> wo) | (wo ? (w1 << (64 - wo)) : 0);
+  const bool round = (win & 1) != 0;
+  uint64_t mant = (win >> 1) & 0xFFFFFFull;
+  if (round && (sticky || (mant & 1))) mant += 1;
+  const float mag = (float)__builtin_ldexp((double)mant, lsb - 298);  // exact in fp32
+  return negr ? -mag : mag;
+}
+
+// Monotone map of fp32 values to unsigned keys (-0 and +0 map alike).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  if (f == 0.0f) f = 0.0f;
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------ scores and top-k
+// Workgroup = R consecutive query blocks of one (batch, query head). Phase 1:
+// each thread scores one candidate KV block against the R pooled query rows
+// (the rows are wave-uniform and come through scalar loads). Phase 2: each
+// wave takes rows and selects the top blocks by bisection on the 32-bit
+// keys, then writes the list in ascending block order.
+template <int D, int R>
+__global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
+  extern __shared__ uint32_t keys_lds[];
+  const int ncand = p.n_cand;
+  const int ncp = (ncand + 63) & ~63;
+  const int i0 = blockIdx.x * R;
+  const int h = blockIdx.y;
+  const int b = blockIdx.z;
+  const int g = h / p.group;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nrows = min(R, p.nq - i0);
+  const double* __restrict__ qrows = p.qp + (((int64_t)b * p.hq + h) * p.nq + i0) * D;
+  const double* __restrict__ qnorm = p.qn + ((int64_t)b * p.hq + h) * p.nq + i0;
+  const float* __restrict__ kcols = p.kpt + ((int64_t)b * p.hkv + g) * D * (int64_t)p.nk;
+  const double* __restrict__ knorm = p.kn + ((int64_t)b * p.hkv + g) * p.nk;
+  const double gamma2 = 2.0 * (double)(D + 2) * 0x1p-53;
+
+  for (int c0 = 0; c0 < ncand; c0 += 256) {
+    const int c = c0 + tid;
+    const bool act = c < ncand;
+    const int j = p.n_prefix_blocks + (act ? c : 0);
+    const float* kc = kcols + j;
+    double acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+    for (int d = 0; d < D; d += 4) {
+      double kd[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kd[u] = (double)kc[(int64_t)(d + u) * p.nk];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const double* qr = qrows + (int64_t)min(r, nrows - 1) * D + d;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[r] = __builtin_fma(qr[u], kd[u], acc[r]);
+      }
+    }
+    if (act) {
+      const double knj = knorm[j];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (r < nrows) {
+          const double s = acc[r];
+          const double w = gamma2 * qnorm[r] * knj + __builtin_fabs(s) * 0x1p-52;
+          const float lo = (float)(s - w);
+          const float hi = (float)(s + w);
+          float f = lo;
+          if (__float_as_uint(lo) != __float_as_uint(hi))
+            f = exact_dot_rn32(qrows + (int64_t)r * D, kc, p.nk, D);
+          keys_lds[r * ncp + c] = order_key(f);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const int rsel = min(p.keep - p.n_forced, ncand);
+  const bool take_all = rsel == ncand;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int M = ncp >> 6;
+  for (int r = wave; r < nrows; r += 4) {
+    const int i = i0 + r;
+    const int64_t row_id = ((int64_t)b * p.hq + h) * p.nq + i;
+    int32_t* out = p.idx + row_id * p.idx_row_stride;
+    const bool row_ok = (int64_t)i * p.bq < (int64_t)p.q_valid;
+    int written = 0;
+    if (row_ok) {
+      const uint32_t* kr = keys_lds + r * ncp;
+      uint32_t thr = 0;
+      int need_eq = 0;
+      if (rsel > 0 && !take_all) {
+        // Largest thr with #{key >= thr} >= rsel: the rsel-th largest key.
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = thr | (1u << bit);
+          int count = 0;
+          for (int m = 0; m < M; ++m) {
+            const int jj = m * 64 + lane;
+            count += __popcll(__ballot(jj < ncand && kr[jj] >= cand));
+          }
+          if (count >= rsel) thr = cand;
+        }
+        int gt = 0;
+        for (int m = 0; m < M; ++m) {
+          const int jj = m * 64 + lane;
+          gt += __popcll(__ballot(jj < ncand && kr[jj] > thr));
+        }
+        need_eq = rsel - gt;  // >= 1
+      }
+      for (int s = lane; s < p.n_forced; s += 64) out[s] = s;
+      int pos = p.n_forced;
+      if (rsel > 0) {
+        int eq_seen = 0;
+        for (int m = 0; m < M; ++m) {
+          const int jj = m * 64 + lane;
+          const bool in = jj < ncand;
+          const uint32_t key = in ? kr[jj] : 0u;
+          const bool gt = in && (take_all || key > thr);
+          const bool eq = in && !take_all && key == thr;
+          const uint64_t eqm = __ballot(eq);
+          const int eq_before = eq_seen + __popcll(eqm & lt_mask);
+          const bool sel = gt || (eq && eq_before < need_eq);
+          const uint64_t selm = __ballot(sel);
+          const int slot = pos + __popcll(selm & lt_mask);
+          if (sel && slot < p.idx_row_stride) out[slot] = p.n_prefix_blocks + jj;
+          pos += __popcll(selm);
+          eq_seen += __popcll(eqm);
+        }
+      }
+      written = pos;
+    }
+    for (int s = written + lane; s < p.idx_row_stride; s += 64) out[s] = -1;
+    if (lane == 0) p.cnt[row_id] = written;
+  }
+}
+
+}  // namespace
+
+int score_rows_per_wg(int n_cand) { return n_cand <= 1024 ? 16 : 8; }
+
+size_t score_lds_bytes(int n_cand) {
+  const size_t ncp = (size_t)((n_cand + 63) & ~63);
+  return (size_t)score_rows_per_wg(n_cand) * ncp * sizeof(uint32_t);
+}
+
+hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t stream) {
+  const dim3 grid(p.nq + p.nk, batch);
+  if (grid.x == 0) return hipSuccess;
+  if (head_dim == 128)
+    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_topk(const ScoreParams& p, int head_dim, int batch, hipStream_t stream) {
+  const int rows = score_rows_per_wg(p.n_cand);
+  const dim3 grid((p.nq + rows - 1) / rows, p.hq, batch);
+  if (grid.x == 0) return hipSuccess;
+  const size_t lds = score_lds_bytes(p.n_cand);
+  // Kernels taking more than 64 KiB of dynamic LDS must say so first.
+  static hipError_t attr_status = []() {
+    const int max_lds = 160 * 1024;
+    const void* fns[4] = {reinterpret_cast<const void*>(&score_topk_kernel<128, 16>),
+                          reinterpret_cast<const void*>(&score_topk_kernel<128, 8>),
+                          reinterpret_cast<const void*>(&score_topk_kernel<64, 16>),
+                          reinterpret_cast<const void*>(&score_topk_kernel<64, 8>)};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }();
+  if (attr_status != hipSuccess) return attr_status;
+  if (head_dim == 128) {
+    if (rows == 16)
+      hipLaunchKernelGGL((score_topk_kernel<128, 16>), grid, dim3(256), lds, stream, p);
+    else
+      hipLaunchKernelGGL((score_topk_kernel<128, 8>), grid, dim3(256), lds, stream, p);
+  } else {
+    if (rows == 16)
+      hipLaunchKernelGGL((score_topk_kernel<64, 16>), grid, dim3(256), lds, stream, p);
+    else
+      hipLaunchKernelGGL((score_topk_kernel<64, 8>), grid, dim3(256), lds, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsattn

@@ -1,0 +1,162 @@
+/*
+ * bsattn.h - C ABI of the selected-block (block-sparse) attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method has two phases (vllm-omni PR #8335 "[Core] Add shared
+ * block-sparse attention adapters with FlashAttention-4", Purpose): a
+ * selector produces, per query head and query block, a list of KV-block
+ * indices and a count; an attention backend then executes exactly that
+ * selection. The protected KV prefix, suffix padding and the native
+ * MHA/MQA/GQA head mapping are part of the contract (same section). Provider
+ * failures propagate: there is no dense fallback and no K/V expansion, under
+ * any condition (same section).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers to tensors are device pointers the caller owns (hipMalloc or a
+ *   framework allocator). The library allocates no memory on any call path.
+ * - Every call is asynchronous on `stream` (0 = the null stream). No call
+ *   synchronises the host, and none copies host memory to the device: all
+ *   metadata travels as kernel arguments.
+ * - q, k, v, out: bf16, 16-byte aligned, head_dim contiguous, element
+ *   strides given per (batch, sequence, head) in `attn_shape`, each a
+ *   multiple of 8.
+ * - block_idx / block_cnt: int32, contiguous, [batch][num_q_heads][NQ][row]
+ *   and [batch][num_q_heads][NQ] with NQ = q_len / block_q and row stride
+ *   `idx_row_stride`.
+ * - lse (optional, may be NULL): fp32, contiguous [batch][num_q_heads][q_len],
+ *   natural-log log-sum-exp of the scaled logits of each query row.
+ * - Arguments are validated on the host before any launch. On error nothing
+ *   is launched, no output is touched, the status is returned and
+ *   attn_last_error() describes the failure (per calling thread).
+ * - Results are deterministic: equal inputs give bitwise equal outputs.
+ *
+ * Sequence layout (diffusers examples/cosmos3/cosmos_parallel.py,
+ * shard_cosmos3_sequence / build_gen_key_mask / cosmos3_cp_attention): the
+ * queries are the generation tokens; the keys and values are the
+ * concatenation of a protected prefix segment and the generation segment,
+ * each padded on its own to a multiple of block_k. Padded keys take no
+ * attention weight; padded query rows produce zero output and lse = -inf.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* inconsistent or out-of-range argument */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  ATTN_ERR_LAUNCH = 4,      /* a kernel launch failed */
+  ATTN_ERR_DEVICE = 5       /* no device, or the current device is not gfx950 */
+} attn_status;
+
+typedef struct attn_shape {
+  int32_t batch;         /* >= 1 */
+  int32_t num_q_heads;   /* Hq >= 1 */
+  int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
+  int32_t head_dim;      /* D in {64, 128} */
+  int32_t block_q;       /* query rows per block, in {64, 128} */
+  int32_t block_k;       /* keys per block, in {64, 128} */
+  int32_t q_len;         /* padded query length, multiple of block_q */
+  int32_t q_valid;       /* real query rows [0, q_valid) */
+  int32_t kv_prefix_len;   /* protected segment [0, kv_prefix_len), multiple of block_k;
+                              its P = kv_prefix_len / block_k blocks are always kept */
+  int32_t kv_prefix_valid; /* real keys [0, kv_prefix_valid) of the prefix segment */
+  int32_t kv_len;          /* padded key length, multiple of block_k, >= kv_prefix_len */
+  int32_t kv_suffix_valid; /* real keys [kv_prefix_len, kv_prefix_len + kv_suffix_valid) */
+  int64_t q_stride[3];   /* element strides of q for (batch, seq, head) */
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+  float softmax_scale;   /* <= 0 selects head_dim ** -0.5 (mstar PR #927, automated review) */
+} attn_shape;
+
+/* Kept KV blocks per query-block row for a target sparsity in percent: the
+ * protected prefix blocks count inside the budget;
+ * clamp(ceil(n_kv_blocks * (100 - sparsity_pct) / 100), n_protected, n_kv_blocks).
+ * The 75 % target of vllm-omni PR #8335 (Purpose) gives 191 of 764 blocks.
+ * Returns -1 if 0 <= n_protected <= n_kv_blocks or 0 <= sparsity_pct <= 100
+ * does not hold. Pure host arithmetic. */
+int32_t attn_keep_blocks(int32_t n_kv_blocks, int32_t n_protected, int32_t sparsity_pct);
+
+/* Bytes of device workspace attn_select_blocks needs for `shape` (pooled
+ * queries and keys and their norms). 0 if the shape is invalid. */
+size_t attn_select_workspace_size(const attn_shape* shape);
+
+/* Block selector (vllm-omni PR #8335, Purpose: per-query-head block indices
+ * and counts; protected KV prefixes).
+ *
+ * For each (batch b, query head h, query block i) with at least one real row:
+ *  1. mean-pool the real rows of the query block and the real keys of every KV
+ *     block of KV head h / (Hq/Hkv): exact sum, one fp64 division, one
+ *     rounding to fp32;
+ *  2. score KV block j as the fp32 value nearest to the exact dot product of
+ *     the two pooled vectors (no softmax scale);
+ *  3. keep every protected block that holds a real key, then the best other
+ *     non-empty blocks by (score descending, index ascending) until
+ *     keep_blocks blocks are kept or none is left.
+ * The pages leave the scoring rule open; block-mean pooling is the reading
+ * this library implements.
+ *
+ * Writes block_idx rows in ascending order, unused slots set to -1, and
+ * block_cnt. Query blocks without a real row get count 0.
+ *
+ * Requirements: P <= keep_blocks <= NK (P = kv_prefix_len / block_k,
+ * NK = kv_len / block_k); idx_row_stride >= keep_blocks; NK <= 4096;
+ * workspace of at least attn_select_workspace_size(shape) bytes, 256-byte
+ * aligned, whose contents are scratch. Real (non-padding) inputs must be
+ * finite; padding may hold anything. */
+attn_status attn_select_blocks(const attn_shape* shape, const void* q, const void* k,
+                               int32_t keep_blocks, int32_t* block_idx, int32_t* block_cnt,
+                               int32_t idx_row_stride, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Block-sparse attention (vllm-omni PR #8335, Purpose: the backend executes
+ * the selection; diffusers cosmos_parallel.py, cosmos3_cp_attention: the
+ * generation pathway's non-causal attention over cat(prefix, gen)).
+ *
+ * For each real query row t of block i of query head h in batch b:
+ *   out[b,t,h,:] = sum_u softmax_u(scale * q.k_u) v_u
+ * over the real keys u of the blocks block_idx[b,h,i,0 .. cnt-1] of KV head
+ * h / (Hq/Hkv), cnt = block_cnt[b,h,i] clamped to [0, idx_row_stride].
+ * bf16 inputs, fp32 accumulation and softmax, bf16 output. Rows with no key
+ * (cnt 0, or only padded keys) and padded rows give 0 and lse -inf. Listed
+ * blocks should be distinct and in [0, NK); entries outside that range are
+ * skipped, the order of the list does not matter. */
+attn_status attn_block_sparse_fwd(const attn_shape* shape, const void* q, const void* k,
+                                  const void* v, const int32_t* block_idx,
+                                  const int32_t* block_cnt, int32_t idx_row_stride, void* out,
+                                  float* lse, hipStream_t stream);
+
+/* Dense attention: attn_block_sparse_fwd with every KV block listed (the
+ * 0 % sparsity case), through the same kernel; no index list is read. */
+attn_status attn_dense_fwd(const attn_shape* shape, const void* q, const void* k, const void* v,
+                           void* out, float* lse, hipStream_t stream);
+
+/* Whether `shape` is supported by the sparse path, checked without touching
+ * the device (vllm-omni PR #8335, Purpose: sparse compatibility is checked
+ * independently of dense-kernel restrictions). ATTN_OK or the error the
+ * entry points would return; attn_last_error() says why. */
+attn_status attn_query_support(const attn_shape* shape);
+
+/* Description of the last failure on the calling thread ("" if none): the
+ * entry point, what failed, the library version and target architecture. */
+const char* attn_last_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,151 @@
+"""C ABI: the library loads without a GPU, exports every function the header
+declares, and rejects bad arguments on the host before touching the device.
+
+Calls here never reach a kernel launch: every argument set fails host-side
+validation. Fake device pointers are used only where validation must fail
+before they could be dereferenced; the module is skipped if a GPU is visible,
+so that a validation bug can never launch a kernel on them."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import block_sparse_attention_blocks_amd as bsa
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+pytestmark = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                                reason="host-validation tests use fake device pointers")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|attn_status|const char\*)\s+(attn_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_three_calls_and_helpers():
+    names = _declared()
+    for n in ("attn_select_blocks", "attn_block_sparse_fwd", "attn_dense_fwd"):
+        assert n in names
+    assert set(names) == set(bsa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(bsa.lib, n)
+
+
+def test_version_and_keep_blocks():
+    assert re.match(r"^\d+\.\d+\.\d+$", bsa.version())
+    assert bsa.lib.attn_keep_blocks(764, 8, 75) == 191
+    assert bsa.lib.attn_keep_blocks(1354, 4, 75) == 339
+    assert bsa.lib.attn_keep_blocks(8, 1, 50) == 4
+    assert bsa.lib.attn_keep_blocks(8, 9, 50) == -1
+    assert bsa.lib.attn_keep_blocks(8, 1, 101) == -1
+
+
+def _layout(**kw):
+    lay = dict(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, block_q=64, block_k=64,
+               q_len=256, q_valid=250, kv_prefix_len=64, kv_prefix_valid=40, kv_len=320,
+               kv_suffix_valid=250, scale=None)
+    lay.update(kw)
+    return lay
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=3), 1),                   # Hq % Hkv != 0
+    (dict(head_dim=96), 2),                     # unsupported head_dim
+    (dict(block_q=32), 2),                      # unsupported geometry
+    (dict(block_k=256), 2),
+    (dict(q_len=250), 1),                       # not a block multiple
+    (dict(q_valid=300), 1),                     # valid > len
+    (dict(kv_prefix_len=40), 1),
+    (dict(kv_prefix_valid=65), 1),
+    (dict(kv_len=300), 1),
+    (dict(kv_suffix_valid=300), 1),
+    (dict(batch=0), 1),
+    (dict(scale=float("nan")), 1),
+])
+def test_shape_validation(kw, status):
+    st, msg = bsa.query_support(_layout(**kw))
+    assert st == status, msg
+    assert "libbsattn" in msg and "gfx950" in msg
+
+
+def test_query_support_ok():
+    assert bsa.query_support(_layout())[0] == 0
+
+
+FAKE = ctypes.c_void_p(1 << 40)          # never dereferenced: validation fails first
+FAKE_MISALIGNED = ctypes.c_void_p((1 << 40) + 4)
+
+
+def _shape(**kw):
+    return ctypes.byref(bsa.make_shape(_layout(**kw)))
+
+
+def test_select_argument_errors():
+    L = bsa.lib
+    ws = L.attn_select_workspace_size(_shape())
+    assert ws > 0
+    # keep below the protected prefix / above NK
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 0, FAKE, FAKE, 8, FAKE, ws, None) == 1
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 6, FAKE, FAKE, 8, FAKE, ws, None) == 1
+    # row stride below keep
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 3, FAKE, FAKE, 2, FAKE, ws, None) == 1
+    # workspace too small / missing / misaligned
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 3, FAKE, FAKE, 3, FAKE, ws - 1, None) == 3
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 3, FAKE, FAKE, 3, None, ws, None) == 3
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 3, FAKE, FAKE, 3,
+                                ctypes.c_void_p((1 << 40) + 16), ws, None) == 3
+    # null / misaligned tensors
+    assert L.attn_select_blocks(_shape(), None, FAKE, 3, FAKE, FAKE, 3, FAKE, ws, None) == 1
+    assert L.attn_select_blocks(_shape(), FAKE_MISALIGNED, FAKE, 3, FAKE, FAKE, 3, FAKE, ws, None) == 2
+    assert L.attn_select_blocks(_shape(), FAKE, FAKE, 3, None, FAKE, 3, FAKE, ws, None) == 1
+    # bad shape
+    assert L.attn_select_blocks(_shape(head_dim=80), FAKE, FAKE, 3, FAKE, FAKE, 3, FAKE, ws, None) == 2
+    assert "keep_blocks" not in bsa.last_error() and "head_dim" in bsa.last_error()
+
+
+def test_attention_argument_errors():
+    L = bsa.lib
+    assert L.attn_block_sparse_fwd(_shape(), FAKE, FAKE, FAKE, None, FAKE, 4, FAKE, None, None) == 1
+    assert L.attn_block_sparse_fwd(_shape(), FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None, None) == 1
+    assert L.attn_block_sparse_fwd(_shape(), FAKE, FAKE, None, FAKE, FAKE, 4, FAKE, None, None) == 1
+    assert L.attn_dense_fwd(_shape(), FAKE, FAKE, FAKE, FAKE_MISALIGNED, None, None) == 2
+    assert L.attn_dense_fwd(_shape(), FAKE, FAKE, FAKE, FAKE,
+                            ctypes.c_void_p((1 << 40) + 2), None) == 1
+    assert L.attn_dense_fwd(_shape(block_q=48), FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    s = bsa.make_shape(_layout())
+    s.k_stride[1] = 260  # not a multiple of 8 elements
+    assert L.attn_dense_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert "k_stride" in bsa.last_error()
+
+
+def test_selector_block_limit():
+    lay = _layout(kv_len=64 * 4200, kv_suffix_valid=64 * 4200 - 64)
+    st, msg = bsa.query_support(lay)
+    assert st == 2 and "4096" in msg
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """Importing the binding with the library absent raises (no CPU fallback)."""
+    import importlib.util
+    import shutil
+    pkg = os.path.join(ROOT, "block_sparse_attention_blocks_amd")
+    dst = tmp_path / "block_sparse_attention_blocks_amd"
+    dst.mkdir()
+    shutil.copy(os.path.join(pkg, "__init__.py"), dst / "__init__.py")
+    spec = importlib.util.spec_from_file_location("bsa_nolib", dst / "__init__.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)

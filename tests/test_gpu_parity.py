@@ -1,0 +1,197 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Selection (indices and counts) must match bit for bit; attention outputs must
+be within max-abs 2e-2 and mean-abs 2e-3 of the oracle over real rows, and
+exactly 0 on padded rows."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_close, case_to_gpu, note, out_to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+bsa = pytest.importorskip("block_sparse_attention_blocks_amd")
+
+
+def _keep(lay, pct):
+    nq, nk, p = bsa.num_blocks(lay)
+    return bsa.keep_blocks(nk, p, pct)
+
+
+def _row_mask(lay):
+    return np.arange(lay["q_len"]) < lay["q_valid"]
+
+
+def _full_check(case, pct, stride_extra=0, check_lse=True):
+    """Select + sparse attention + dense attention on the GPU vs the oracle."""
+    lay = case.layout
+    keep = _keep(lay, pct)
+    note(f"[gpu] {case.name} {lay} keep={keep}")
+    q, k, v = case_to_gpu(case)
+    idx, cnt = bsa.select_blocks(q, k, lay, keep, keep + stride_extra)
+    out, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, return_lse=True)
+    dense, dlse = bsa.dense_attention(q, k, v, lay, return_lse=True)
+    torch.cuda.synchronize()
+    ridx, rcnt = oracle.select(lay, case.q, case.k, keep, idx_row_stride=keep + stride_extra)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert np.array_equal(gc, rcnt), "block counts differ"
+    assert np.array_equal(gi, ridx), f"block indices differ at {np.argwhere(gi != ridx)[:5]}"
+    ro, rl = oracle.attend(lay, case.q, case.k, case.v, ridx, rcnt)
+    rd, rdl = oracle.dense(lay, case.q, case.k, case.v)
+    rows = _row_mask(lay)
+    for name, got, ref in (("sparse", out, ro), ("dense", dense, rd)):
+        g = out_to_f64(got)
+        assert_close(g[:, rows], ref[:, rows], what=name)
+        assert (g[:, ~rows] == 0).all(), f"{name}: padded rows not zero"
+    if check_lse:
+        for got, ref in ((lse, rl), (dlse, rdl)):
+            g = got.cpu().numpy().astype(np.float64)
+            fin = np.isfinite(ref)
+            assert np.array_equal(np.isfinite(g), fin)
+            assert np.abs(g[fin] - ref[fin]).max() < 1e-3
+    return idx, cnt, out, dense
+
+
+def test_tiny_config():
+    _full_check(synth.make_config("tiny"), 50)
+
+
+@pytest.mark.parametrize("name,kw,pct", [
+    ("gqa_ragged_d128", dict(hq=4, hkv=2, d=128, prefix=100, gen=300, cfg=41), 60),
+    ("mha_d64_bq128", dict(hq=2, hkv=2, d=64, bq=128, bk=64, prefix=64, gen=700, cfg=42), 50),
+    ("mqa_bk128", dict(hq=3, hkv=1, d=128, bq=64, bk=128, prefix=200, gen=900, cfg=43), 50),
+    ("b2_bq128_bk128", dict(batch=2, hq=4, hkv=1, d=128, bq=128, bk=128, prefix=130, gen=1000,
+                            cfg=44), 75),
+    ("lowrank", dict(hq=4, hkv=2, d=128, prefix=512, gen=1560, frames=(1, 30, 52),
+                     dist="lowrank", cfg=45), 75),
+    ("no_prefix", dict(hq=2, hkv=1, d=128, prefix=0, gen=500, cfg=46), 75),
+    ("one_key", dict(hq=2, hkv=1, d=64, prefix=0, gen=1, cfg=47), 0),
+    ("int_ties", dict(hq=2, hkv=1, d=64, prefix=64, gen=448, dist="int", int_range=1, cfg=48), 50),
+])
+def test_shapes_and_edges(name, kw, pct):
+    _full_check(synth.make_case(name, **kw), pct, stride_extra=3)
+
+
+def test_exact_score_fallback_path():
+    """Scores whose fp64 dot product is inexact near an fp32 rounding
+    boundary go through the exact accumulator; indices must still match."""
+    case = synth.make_case("cancel", dist="cancel", hq=4, hkv=2, d=128, prefix=128, gen=1920,
+                           cfg=49)
+    lay = case.layout
+    keep = _keep(lay, 60)
+    _, _, sc, nfb = oracle.select(lay, case.q, case.k, keep, return_scores=True)
+    assert nfb > 100  # the oracle itself needed exact sums here
+    q, k, _ = case_to_gpu(case)
+    idx, cnt = bsa.select_blocks(q, k, lay, keep)
+    ridx, rcnt = oracle.select(lay, case.q, case.k, keep)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
+def test_dense_equals_sparse_with_all_blocks_bitwise():
+    case = synth.make_case("allblocks", hq=4, hkv=2, d=128, prefix=100, gen=700, cfg=50)
+    lay = case.layout
+    q, k, v = case_to_gpu(case)
+    nq, nk, p = bsa.num_blocks(lay)
+    idx, cnt = bsa.select_blocks(q, k, lay, nk)
+    a = bsa.block_sparse_attention(q, k, v, idx, cnt, lay)
+    b = bsa.dense_attention(q, k, v, lay)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_run_twice_bitwise():
+    case = synth.make_case("twice", hq=4, hkv=2, d=128, prefix=512, gen=1560, frames=(1, 30, 52),
+                           dist="lowrank", cfg=51)
+    lay = case.layout
+    q, k, v = case_to_gpu(case)
+    keep = _keep(lay, 75)
+    r = []
+    for _ in range(2):
+        idx, cnt = bsa.select_blocks(q, k, lay, keep)
+        o = bsa.block_sparse_attention(q, k, v, idx, cnt, lay)
+        torch.cuda.synchronize()
+        r.append((idx.clone(), cnt.clone(), o.clone()))
+    assert torch.equal(r[0][0], r[1][0]) and torch.equal(r[0][1], r[1][1])
+    assert torch.equal(r[0][2].view(torch.int16), r[1][2].view(torch.int16))
+
+
+@pytest.mark.parametrize("fill", [float("nan"), 1.0e4])
+def test_padding_contents_do_not_matter(fill):
+    kw = dict(hq=4, hkv=2, d=128, prefix=100, gen=300, cfg=52)
+    base = synth.make_case("pad0", **kw)
+    dirty = synth.make_case("padx", pad_fill=fill, **kw)
+    lay = base.layout
+    keep = _keep(lay, 50)
+    outs = []
+    for c in (base, dirty):
+        q, k, v = case_to_gpu(c)
+        idx, cnt = bsa.select_blocks(q, k, lay, keep)
+        o = bsa.block_sparse_attention(q, k, v, idx, cnt, lay)
+        d = bsa.dense_attention(q, k, v, lay)
+        torch.cuda.synchronize()
+        outs.append((idx, cnt, o, d))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    for j in (2, 3):
+        assert torch.equal(outs[0][j].view(torch.int16), outs[1][j].view(torch.int16))
+
+
+def test_list_order_and_out_of_range_entries():
+    case = synth.make_case("order", hq=2, hkv=1, d=128, prefix=64, gen=448, cfg=53)
+    lay = case.layout
+    q, k, v = case_to_gpu(case)
+    keep = _keep(lay, 50)
+    idx, cnt = bsa.select_blocks(q, k, lay, keep, keep + 2)
+    ref = bsa.block_sparse_attention(q, k, v, idx, cnt, lay)
+    # reversed lists, with two out-of-range entries appended inside the count
+    rev = idx.clone()
+    rev[..., :keep] = torch.flip(idx[..., :keep], dims=[-1])
+    rev[..., keep] = -1
+    rev[..., keep + 1] = 10 ** 6
+    o = bsa.block_sparse_attention(q, k, v, rev, cnt + 2, lay)
+    torch.cuda.synchronize()
+    d = (o.float() - ref.float()).abs()
+    assert float(d.max()) < 1e-2 and float(d.mean()) < 1e-3
+
+
+def test_empty_and_degenerate_layouts():
+    # every query row is padding: counts 0, outputs 0
+    case = synth.make_case("nopad", hq=2, hkv=1, d=128, prefix=64, gen=448, cfg=54)
+    lay = dict(case.layout, q_valid=0)
+    q, k, v = case_to_gpu(case)
+    idx, cnt = bsa.select_blocks(q, k, lay, 4)
+    o, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, return_lse=True)
+    torch.cuda.synchronize()
+    assert int(cnt.abs().sum()) == 0 and bool((idx == -1).all())
+    assert float(o.float().abs().max()) == 0.0 and bool(torch.isinf(lse).all())
+    # no real key at all: outputs 0 and lse -inf, counts 0
+    lay2 = dict(case.layout, kv_prefix_valid=0, kv_suffix_valid=0)
+    idx, cnt = bsa.select_blocks(q, k, lay2, 1)
+    o, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay2, return_lse=True)
+    d, dl = bsa.dense_attention(q, k, v, lay2, return_lse=True)
+    torch.cuda.synchronize()
+    assert int(cnt.sum()) == 0
+    for t, l in ((o, lse), (d, dl)):
+        assert float(t.float().abs().max()) == 0.0 and bool(torch.isinf(l).all())
+    # no keys at all (kv_len 0): keep must be 0
+    lay3 = dict(case.layout, kv_prefix_len=0, kv_prefix_valid=0, kv_len=0, kv_suffix_valid=0)
+    idx, cnt = bsa.select_blocks(q, k, lay3, 0, 1)
+    d = bsa.dense_attention(q, k, v, lay3)
+    torch.cuda.synchronize()
+    assert int(cnt.sum()) == 0 and float(d.float().abs().max()) == 0.0
+    # no query rows at all (q_len 0): nothing to do, no error
+    lay4 = dict(case.layout, q_len=0, q_valid=0)
+    bsa.dense_attention(q, k, v, lay4, out=torch.empty_like(q))
+
+
+def test_errors_propagate_from_the_binding():
+    case = synth.make_config("tiny")
+    q, k, v = case_to_gpu(case)
+    lay = dict(case.layout, num_kv_heads=3)
+    with pytest.raises(bsa.BsAttnError, match="INVALID_ARG"):
+        bsa.dense_attention(q, k, v, lay)
+    with pytest.raises(bsa.BsAttnError, match="keep_blocks"):
+        bsa.select_blocks(q, k, case.layout, 0)
