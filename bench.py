@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=756)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device copy of BYTES bytes (a known-size kernel "
+                         "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -157,6 +160,13 @@ def main():
         bsa.block_sparse_attention(q, k, v, idx, cnt, lay, out=outs[s], stream=stream)
         if ev is not None:
             ev[2].record(stream)
+
+    if args.calibrate_copy > 0:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # Warm up every layout (each input set) before timing.
     for w in range(max(args.warmup, len(sets))):

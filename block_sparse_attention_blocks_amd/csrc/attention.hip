@@ -56,45 +56,112 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(imm);
 }
 
-// Issue the HBM->LDS copy of one [BK x D] bf16 tile. `src` points at row 0 of
-// the tile for the right batch and KV head; rows are `row_stride` elements
-// apart. Each wave instruction moves 64 x 16 bytes = RPI whole rows.
-template <int D, int BK, int NW>
-__device__ __forceinline__ void issue_tile(const uint16_t* src, int64_t row_stride, uint16_t* lds,
-                                           int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int RPI = 64 / CPR;
-  constexpr int NL = BK / (NW * RPI);
-  static_assert(NL * NW * RPI == BK, "tile split");
-  const int rsub = lane / CPR;
-  const int pch = lane % CPR;
-#pragma unroll
-  for (int it = 0; it < NL; ++it) {
-    const int rbase = (it * NW + wave) * RPI;
-    const int row = rbase + rsub;
-    const int lch = pch ^ swz<CPR>(row);
-    const uint16_t* g = src + (int64_t)row * row_stride + lch * 8;
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                     (__attribute__((address_space(3))) void*)(lds + rbase * D),
-                                     16, 0, 0);
-  }
+// Workgroup barrier that orders LDS accesses only. Unlike __syncthreads()
+// it does not wait for outstanding HBM->LDS copies, which stay in flight
+// across it; their completion is awaited explicitly with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
+// HBM->LDS copy of one [BK x D] bf16 tile with global_load_lds_dwordx4 in its
+// scalar-base form: the LDS destination comes from M0 and the HBM address is
+// a 64-bit scalar base plus a 32-bit per-lane offset, so issuing a copy costs
+// no vector ALU work. Each wave instruction moves 64 x 16 bytes = RPI whole
+// rows; instruction `it` of wave `wave` fills rows (it * NW + wave) * RPI +
+// [0, RPI). The row step between instructions is a multiple of 8 rows, so the
+// XOR swizzle of a lane's chunk is the same for every instruction and the
+// per-lane offset is fixed for the whole kernel.
+//
+// The copies are issued from inline assembly, so the compiler does not track
+// them: every read of a tile is preceded by an explicit wait_vmcnt on the
+// copies that must have landed and an LDS barrier.
+template <int D, int BK, int NW>
+struct TileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int NL = BK / (NW * RPI);
+  static_assert(NL * NW * RPI == BK, "tile split");
+  static_assert((NW * RPI) % 8 == 0, "instruction row step must keep the swizzle");
+  uint32_t voff;        // per-lane byte offset inside the tile
+  uint32_t step_bytes;  // uniform byte step between two instructions
+  uint32_t lds_base;    // uniform LDS byte address of this wave's first rows
+
+  __device__ __forceinline__ void init(int64_t row_stride, int wave, int lane, const uint16_t* lds) {
+    const int row = wave * RPI + lane / CPR;
+    const int lch = (lane % CPR) ^ swz<CPR>(row);
+    voff = (uint32_t)((row * row_stride + lch * 8) * 2);
+    step_bytes = (uint32_t)(NW * RPI * row_stride * 2);
+    lds_base = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)lds) +
+               (uint32_t)(wave * RPI * D * 2);
+  }
+  // `tile` is the uniform address of row 0 of the tile.
+  __device__ __forceinline__ void issue(const uint16_t* tile) const {
+#pragma unroll
+    for (int it = 0; it < NL; ++it) {
+      const char* g = reinterpret_cast<const char*>(tile) + (size_t)it * step_bytes;
+      const uint32_t m0v = lds_base + (uint32_t)(it * NW * RPI * D * 2);
+      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :
+                   : "v"(voff), "s"(g), "s"(m0v)
+                   : "memory", "m0");
+    }
+  }
+};
+
+// Uniform 32-bit load through the scalar data cache (the index list is
+// read-only here); waits for its own completion.
+__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+// Value of the other half-wave: lanes l and l ^ 32 hold the same query row.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Wait until at most k tile copies (NL instructions each) are still in flight.
+template <int NL>
+__device__ __forceinline__ void wait_tiles(int k) {
+  if (k <= 0)
+    wait_vmcnt<0>();
+  else
+    wait_vmcnt<NL>();
+}
+
+// Kernel body. One wave per 32 query rows; the keys of each listed KV block
+// are processed as sub-tiles of 64 keys. Per sub-tile u the step is
+//   [wait K of u+1] S[u+1] = K Q^T on the matrix cores, interleaved with the
+//   softmax of S[u] on the vector ALUs; [issue next K] [wait V of u]
+//   O += V^T P[u]^T; [issue next V]
+// so the exponentials of one sub-tile hide under the QK^T products of the
+// next. K and V tiles are single-buffered in LDS; the copy of block n+2's K
+// overlaps the PV of block n and the copy of block n+1's V overlaps the QK^T
+// and softmax of block n+1.
 template <int D, int BQ, int BK, bool DENSE>
-__global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
-attn_fwd_kernel(const AttnParams p) {
+__device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ Ks,
+                                              uint16_t* __restrict__ Vs) {
   constexpr int NW = BQ / 32;
   constexpr int CPR = D / 8;
-  constexpr int RPI = 64 / CPR;
-  constexpr int NL = BK / (NW * RPI);  // copy instructions per thread per tile
-  constexpr int KS = D / 16;           // MFMA k-steps over D
-  constexpr int DT = D / 32;           // output 32-row tiles over D
-  constexpr int KT = BK / 32;          // 32-key sub-tiles per block
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * D];
+  constexpr int KS = D / 16;  // MFMA k-steps over D
+  constexpr int DT = D / 32;  // output 32-row tiles over D
+  constexpr int SUB = 64;     // keys per pipeline sub-tile
+  constexpr int KT = SUB / 32; // 32-key MFMA tiles per sub-tile
+  constexpr int SPB = BK / SUB; // sub-tiles per KV block
+  using Copy = TileCopy<D, BK, NW>;
+  constexpr int NL = Copy::NL;
+  // A row moves its reference max only when a sub-tile max exceeds it by
+  // more than this many powers of two; until then probabilities are taken
+  // against the stale max and stay below 2^8, far from fp32 or bf16 overflow.
+  constexpr float kRescaleSlack = 8.0f;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 31;
   const int half = lane >> 5;
 
@@ -130,19 +197,24 @@ attn_fwd_kernel(const AttnParams p) {
     nblk = p.n_forced + p.n_cand;
   } else {
     const int64_t row_id = ((int64_t)b * p.hq + h) * p.nq + i;
-    nblk = min(max(p.cnt[row_id], 0), p.idx_row_stride);
+    nblk = min(max(scalar_load_i32(p.cnt + row_id), 0), p.idx_row_stride);
     idx_row = p.idx + row_id * p.idx_row_stride;
   }
-  if (row0 >= p.q_valid) nblk = 0;
+  if (row0 >= p.q_valid || p.nk == 0) nblk = 0;
 
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
+  Copy kcopy, vcopy;
+  kcopy.init(p.ks1, wave, lane, Ks);
+  vcopy.init(p.vs1, wave, lane, Vs);
 
+  // Listed block n. Entries outside [0, NK) are copied from block 0 (always
+  // in bounds) with no real key, which gives them zero weight.
   auto block_of = [&](int n) -> int {
     if constexpr (DENSE) {
       return n < p.n_forced ? n : p.n_prefix_blocks + (n - p.n_forced);
     } else {
-      return idx_row[n];
+      return scalar_load_i32(idx_row + n);
     }
   };
   // Real keys of block j form a prefix [0, nvalid) of the block: segments
@@ -154,154 +226,213 @@ attn_fwd_kernel(const AttnParams p) {
         (s0 < p.kv_prefix_len) ? p.kv_prefix_valid : p.kv_prefix_len + p.kv_suffix_valid;
     return min(max(seg_end - s0, 0), BK);
   };
+  auto load_of = [&](int j) -> int64_t { return (j < 0 || j >= p.nk) ? 0 : (int64_t)j * BK; };
 
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
+  // Row sums of P come out of the matrix core: ones(32 x 16) x P^T puts the
+  // sum over a 16-key step into every row of the accumulator (one query per
+  // lane); entry 0 is the one kept.
+  f32x16 lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  float m_run = -__builtin_inff();  // reference max (log2 units) of this row
   const float sl2 = p.scale_log2;
 
-  // LDS read offsets that do not depend on the block.
+  // LDS element offsets that do not depend on the block.
+  const int sw = swz<CPR>(col);  // swizzle of K rows kt*32 + col
+  int koffs[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koffs[ks] = col * D + (((2 * ks + half) ^ sw) << 3);
   const int g16 = lane >> 4, j16 = lane & 15, tq = j16 >> 2, q4 = j16 & 3;
+  int voffs[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int d = dt * 32 + 16 * (g16 & 1) + 4 * q4;
+      const int row = 8 * c2 + 4 * half + tq;  // + multiples of 16
+      voffs[dt][c2] = row * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
+    }
 
-  int j_cur = -1, nv_cur = 0;
+  // S = K Q^T for sub-tile `sub` of the K tile in LDS.
+  auto qk = [&](f32x16 (&sd)[KT], int sub) {
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sd[kt][r] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(Ks + (sub * SUB + kt * 32) * D + koffs[ks]);
+        sd[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sd[kt], 0, 0, 0);
+      }
+    }
+  };
+
+  // Pipeline state (blocks): block n is being finished, block n+1 is next.
+  int j1 = -1, nv1 = 0;  // block n+1
+  int j2 = -1, nv2 = 0;  // block n+2
+  int nv0 = 0;           // block n
+  f32x16 sA[KT], sB[KT];
+
   if (nblk > 0) {
-    j_cur = block_of(0);
-    nv_cur = nvalid_of(j_cur);
-    if (nv_cur > 0) {
-      issue_tile<D, BK, NW>(kbase + (int64_t)j_cur * BK * p.ks1, p.ks1, Ks, wave, lane);
-      issue_tile<D, BK, NW>(vbase + (int64_t)j_cur * BK * p.vs1, p.vs1, Vs, wave, lane);
+    const int j0 = block_of(0);
+    nv0 = nvalid_of(j0);
+    kcopy.issue(kbase + load_of(j0) * p.ks1);
+    vcopy.issue(vbase + load_of(j0) * p.vs1);
+    wait_tiles<NL>(1);  // K[0] landed (V[0] may be in flight)
+    lds_barrier();
+    qk(sA, 0);
+    if (nblk > 1) {
+      j1 = block_of(1);
+      nv1 = nvalid_of(j1);
+    }
+    if constexpr (SPB == 1) {
+      lds_barrier();
+      if (nblk > 1) kcopy.issue(kbase + load_of(j1) * p.ks1);
     }
   }
 
-  for (int n = 0; n < nblk; ++n) {
-    int j_nxt = -1, nv_nxt = 0;
-    if (n + 1 < nblk) {
-      j_nxt = block_of(n + 1);
-      nv_nxt = nvalid_of(j_nxt);
+  // One pipeline step on sub-tile `sub` of block n; s_cur holds its S,
+  // s_nxt receives the S of the next sub-tile.
+  auto step = [&](int n, int sub, f32x16 (&s_cur)[KT], f32x16 (&s_nxt)[KT]) {
+    const bool last_sub = sub == SPB - 1;
+    const bool has_next = !last_sub || n + 1 < nblk;
+    if (last_sub && n + 2 < nblk) {
+      j2 = block_of(n + 2);
+      nv2 = nvalid_of(j2);
     }
-    f32x16 s[KT];
-    if (nv_cur > 0) {
-      wait_vmcnt<NL>();  // K of this block has landed (its V may still be in flight)
-      __syncthreads();
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
-        const int row = kt * 32 + col;
-        const uint16_t* krow = Ks + row * D;
-        const int sw = swz<CPR>(row);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch = (2 * ks + half) ^ sw;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + ch * 8);
-          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with the K tile
-    if (nv_nxt > 0)
-      issue_tile<D, BK, NW>(kbase + (int64_t)j_nxt * BK * p.ks1, p.ks1, Ks, wave, lane);
-
-    if (nv_cur > 0) {
-      // ---- online softmax on S^T: lane owns query col, keys
-      //      kt*32 + (r/4)*8 + half*4 + r%4.
-      if (nv_cur < BK) {
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-            if (key >= nv_cur) s[kt][r] = -__builtin_inff();
-          }
-      }
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kt][r]);
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = __builtin_fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float rs = 0.0f;
+    // Padded keys of this sub-tile get -inf.
+    const int nvs = nv0 - sub * SUB;  // real keys of this sub-tile (may be <= 0)
+    if (nvs < SUB) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], sl2, -m_use));
-          s[kt][r] = e;
-          rs += e;
+          const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
+          if (key >= nvs) s_cur[kt][r] = -__builtin_inff();
         }
-      rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+    }
+    if (last_sub && has_next) {
+      // K of block n+1 must have landed. With one sub-tile per block it was
+      // issued before V of block n (n = 0) or after it; with two it was
+      // issued in this block's first step and nothing followed it.
+      wait_tiles<NL>((SPB == 1 && n >= 1) ? 1 : 0);
+      lds_barrier();
+    }
+
+    // ---- S of the next sub-tile on the matrix cores || softmax of S[cur].
+    if (has_next) qk(s_nxt, last_sub ? 0 : sub + 1);
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_cur[kt][r], s_cur[kt][r + 1]));
+    mx = max_with_other_half(mx) * sl2;
+    const bool need = mx > m_run + kRescaleSlack;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+    m_run = need ? mx : m_run;
+    const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+    bf16x8 pf[2 * KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          pf[2 * kt + s2][e] =
+              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][8 * s2 + e], sl2, -m_use));
+    if (has_next) {
+#pragma unroll
+      for (int k = 0; k < KS * KT; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      }
+    }
+
+    // Lazy rescale of the running output (rare after the first sub-tiles).
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      lacc[0] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
 
-      // P^T as the B operand: k-step (kt, s2) takes accumulator entries
-      // r = 8 s2 .. 8 s2 + 7, i.e. keys kt*32 + 16 s2 + {4 half + 0..3, 8 + 4 half + 0..3}.
-      bf16x8 pf[2 * KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[2 * kt + s2][e] = (__bf16)s[kt][8 * s2 + e];
-
-      if (nv_nxt > 0)
-        wait_vmcnt<NL>();  // V of this block has landed (next K may be in flight)
-      else
-        wait_vmcnt<0>();
-      __syncthreads();
-      if (nv_cur < BK) {
+    // The K tile is free once the last sub-tile of the block it holds has
+    // been multiplied: with one sub-tile per block that happened just now for
+    // block n+1 (refill with n+2), with two it happened in the first step of
+    // block n (refill with n+1).
+    if constexpr (SPB == 1) {
+      lds_barrier();
+      if (n + 2 < nblk) kcopy.issue(kbase + load_of(j2) * p.ks1);
+    } else {
+      if (sub == SPB - 2) {
+        lds_barrier();
+        if (n + 1 < nblk) kcopy.issue(kbase + load_of(j1) * p.ks1);
+      }
+    }
+    if (sub == 0) {
+      // V of block n; the K copy issued just above may still be in flight.
+      wait_tiles<NL>((SPB == 1 ? n + 2 < nblk : n + 1 < nblk) ? 1 : 0);
+      lds_barrier();
+      if (nv0 < BK) {
         // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows.
         constexpr int NT = NW * 64;
-        uint4* vz = reinterpret_cast<uint4*>(Vs + nv_cur * D);
-        const int nz = (BK - nv_cur) * D / 8;
+        uint4* vz = reinterpret_cast<uint4*>(Vs + nv0 * D);
+        const int nz = (BK - nv0) * D / 8;
         for (int e = threadIdx.x; e < nz; e += NT) vz[e] = make_uint4(0, 0, 0, 0);
-        __syncthreads();
+        lds_barrier();
       }
-
-      // ---- O^T += V^T P^T. V^T fragment of lane: row d = dt*32 + col,
-      //      k-slots 0..3 / 4..7 = keys base + 0..3 / base + 8 + 0..3 with
-      //      base = kt*32 + 16 s2 + 4 half; one transpose read per group of 4.
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            bf16x4 v0, v1;
-            const int d = dt * 32 + 16 * (g16 & 1) + 4 * q4;
-            {
-              const int row = kt * 32 + 16 * s2 + 4 * half + tq;
-              const int off = row * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
-              v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + off));
-            }
-            {
-              const int row = kt * 32 + 16 * s2 + 8 + 4 * half + tq;
-              const int off = row * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
-              v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + off));
-            }
-            const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[2 * kt + s2], o[dt], 0, 0, 0);
-          }
-        }
     }
-    __syncthreads();  // every wave is done with the V tile
-    if (nv_nxt > 0)
-      issue_tile<D, BK, NW>(vbase + (int64_t)j_nxt * BK * p.vs1, p.vs1, Vs, wave, lane);
-    j_cur = j_nxt;
-    nv_cur = nv_nxt;
+
+    // ---- O^T += V^T P^T. V^T fragment of lane: row d = dt*32 + col,
+    //      k-slots 0..3 / 4..7 = keys base + 0..3 / base + 8 + 0..3 with
+    //      base = 32 kt + 16 s2 + 4 half; one transpose read per group of 4.
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int kb = (sub * SUB + kt * 32 + 16 * s2) * D;
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[2 * kt + s2], lacc, 0, 0, 0);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const bf16x4 v0 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + kb + voffs[dt][0]));
+          const bf16x4 v1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + kb + voffs[dt][1]));
+          const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[2 * kt + s2], o[dt], 0, 0, 0);
+        }
+      }
+    if (last_sub) {
+      lds_barrier();  // every wave is done with the V tile
+      if (n + 1 < nblk) vcopy.issue(vbase + load_of(j1) * p.vs1);
+      nv0 = nv1;
+      j1 = j2;
+      nv1 = nv2;
+    }
+  };
+
+  // Sub-tiles in order, two per loop turn so that the S registers alternate
+  // statically between sA and sB.
+  const int nsub = nblk * SPB;
+  for (int u = 0; u < nsub; u += 2) {
+    step(u / SPB, u % SPB, sA, sB);
+    if (u + 1 < nsub) step((u + 1) / SPB, (u + 1) % SPB, sB, sA);
   }
 
   // ---- epilogue: O^T lane layout is query col, d = dt*32 + (r/4)*8 + half*4 + r%4.
+  const float l_run = lacc[0];
   const bool row_ok = qrow < p.q_valid && l_run > 0.0f;
   const float inv = row_ok ? 1.0f / l_run : 0.0f;
   uint16_t* op = p.o + (int64_t)b * p.os0 + (int64_t)qrow * p.os1 + (int64_t)h * p.os2;
@@ -319,6 +450,14 @@ attn_fwd_kernel(const AttnParams p) {
                              : -__builtin_inff();
     p.lse[((int64_t)b * p.hq + h) * p.q_len + qrow] = lse;
   }
+}
+
+template <int D, int BQ, int BK, bool DENSE>
+__global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
+attn_fwd_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * D];
+  attn_fwd_body<D, BQ, BK, DENSE>(p, Ks, Vs);
 }
 
 template <int D, int BQ, int BK, bool DENSE>
