@@ -29,6 +29,14 @@ HIP_FLAGS = [
 ]
 
 
+# The attention kernel never relies on NaN semantics (padded keys are masked
+# by index and padded V rows are cleared), so its max reductions may skip the
+# NaN quieting that IEEE max would otherwise add before each v_max3. Its MFMA
+# results are consumed by vector ALU code, so they are kept in ordinary VGPRs
+# (no accumulation-register round trips).
+FILE_FLAGS = {"attention.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -57,7 +65,8 @@ def build(verbose: bool = False) -> str:
         for src in srcs:
             obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
             objs.append(obj)
-            cmd = [hipcc, *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+            extra = FILE_FLAGS.get(os.path.basename(src), [])
+            cmd = [hipcc, *HIP_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
             jobs.append((src, ex.submit(_run, cmd)))
         for src, fut in jobs:
             rc, out = fut.result()

@@ -30,6 +30,8 @@
 //    range of (KV head, query block), keeping that range's K/V tiles in the
 //    XCD's L2.
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace bsattn {
@@ -41,9 +43,21 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // Chunk permutation of row `row` in an LDS tile with CPR 16-byte chunks.
+// LDS serves 256 contiguous bytes per cycle. With 16 chunks per row (head
+// dim 128) the permutation 4 (r % 4) + (r / 4) % 4 gives
+//  * the K reads (16 lanes = 16 consecutive rows, one chunk each) 16
+//    distinct chunk positions, and
+//  * the V transpose reads (32 lanes = 4 consecutive rows x 4 adjacent
+//    chunks) 16 distinct chunk positions.
+// With 8 chunks per row two rows share a 256-byte line, and (r / 2) % 8
+// keeps the K reads conflict-free.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
-  return ((row & 7) << 1) & (CPR - 1);
+  if constexpr (CPR == 16) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    return (row >> 1) & (CPR - 1);
+  }
 }
 
 // Wait until at most N vector-memory operations of this wave are in flight
@@ -83,28 +97,36 @@ struct TileCopy {
   static constexpr int RPI = 64 / CPR;
   static constexpr int NL = BK / (NW * RPI);
   static_assert(NL * NW * RPI == BK, "tile split");
-  static_assert((NW * RPI) % 8 == 0, "instruction row step must keep the swizzle");
-  uint32_t voff;        // per-lane byte offset inside the tile
+  static_assert((NW * RPI) % 8 == 0, "the swizzle must repeat every two instructions");
+  uint32_t voff[2];     // per-lane byte offset inside the tile, by instruction parity
   uint32_t step_bytes;  // uniform byte step between two instructions
   uint32_t lds_base;    // uniform LDS byte address of this wave's first rows
 
   __device__ __forceinline__ void init(int64_t row_stride, int wave, int lane, const uint16_t* lds) {
-    const int row = wave * RPI + lane / CPR;
-    const int lch = (lane % CPR) ^ swz<CPR>(row);
-    voff = (uint32_t)((row * row_stride + lch * 8) * 2);
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = (par * NW + wave) * RPI + lane / CPR;
+      const int lch = (lane % CPR) ^ swz<CPR>(row);
+      voff[par] = (uint32_t)((row * row_stride + lch * 8) * 2 - par * NW * RPI * row_stride * 2);
+    }
     step_bytes = (uint32_t)(NW * RPI * row_stride * 2);
     lds_base = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)lds) +
                (uint32_t)(wave * RPI * D * 2);
   }
-  // `tile` is the uniform address of row 0 of the tile.
-  __device__ __forceinline__ void issue(const uint16_t* tile) const {
+  // `tile` is the uniform address of row 0 of the tile; `lds_off` selects
+  // the LDS buffer (bytes). The uniform address arithmetic is redone at each
+  // call (the empty asm statements hide the loop-invariant parts from
+  // hoisting), which keeps scalar registers free.
+  __device__ __forceinline__ void issue(const uint16_t* tile, uint32_t lds_off = 0) const {
+    uint32_t step = step_bytes, lbase = lds_base + lds_off;
+    asm volatile("" : "+s"(step), "+s"(lbase));
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const char* g = reinterpret_cast<const char*>(tile) + (size_t)it * step_bytes;
-      const uint32_t m0v = lds_base + (uint32_t)(it * NW * RPI * D * 2);
+      const char* g = reinterpret_cast<const char*>(tile) + (size_t)(it * step);
+      const uint32_t m0v = lbase + (uint32_t)(it * NW * RPI * D * 2);
       asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                    :
-                   : "v"(voff), "s"(g), "s"(m0v)
+                   : "v"(voff[it & 1]), "s"(g), "s"(m0v)
                    : "memory", "m0");
     }
   }
@@ -125,36 +147,32 @@ __device__ __forceinline__ float max_with_other_half(float x) {
   return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Wait until at most k tile copies (NL instructions each) are still in flight.
-template <int NL>
-__device__ __forceinline__ void wait_tiles(int k) {
-  if (k <= 0)
-    wait_vmcnt<0>();
-  else
-    wait_vmcnt<NL>();
-}
-
 // Kernel body. One wave per 32 query rows; the keys of each listed KV block
-// are processed as sub-tiles of 64 keys. Per sub-tile u the step is
-//   [wait K of u+1] S[u+1] = K Q^T on the matrix cores, interleaved with the
-//   softmax of S[u] on the vector ALUs; [issue next K] [wait V of u]
-//   O += V^T P[u]^T; [issue next V]
-// so the exponentials of one sub-tile hide under the QK^T products of the
-// next. K and V tiles are single-buffered in LDS; the copy of block n+2's K
-// overlaps the PV of block n and the copy of block n+1's V overlaps the QK^T
-// and softmax of block n+1.
+// are processed as sub-tiles of 64 keys. K and V tiles are double-buffered in
+// LDS and each step starts with the only workgroup barrier of the step: the
+// copies issued one step earlier have landed and the buffers read in the
+// previous step are free for the next copies. Per sub-tile u a wave then runs
+//   (a) S[u+1] = K Q^T on the matrix cores, interleaved instruction by
+//       instruction with the exponentials of P[u] (the row maxima of S[u]
+//       are already known) and the V transpose reads for step (b);
+//   (b) O += V^T P[u]^T and the row sums of P[u] on the matrix cores,
+//       interleaved with the masking and row maxima of S[u+1].
+// One wave per SIMD: the matrix cores and the vector ALUs are kept busy by
+// the interleaving inside the wave rather than by switching waves.
 template <int D, int BQ, int BK, bool DENSE>
 __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ Ks,
                                               uint16_t* __restrict__ Vs) {
   constexpr int NW = BQ / 32;
   constexpr int CPR = D / 8;
-  constexpr int KS = D / 16;  // MFMA k-steps over D
-  constexpr int DT = D / 32;  // output 32-row tiles over D
-  constexpr int SUB = 64;     // keys per pipeline sub-tile
-  constexpr int KT = SUB / 32; // 32-key MFMA tiles per sub-tile
+  constexpr int KS = D / 16;    // MFMA k-steps over D
+  constexpr int DT = D / 32;    // output 32-row tiles over D
+  constexpr int SUB = 64;       // keys per pipeline sub-tile
+  constexpr int KT = SUB / 32;  // 32-key MFMA tiles per sub-tile
   constexpr int SPB = BK / SUB; // sub-tiles per KV block
+  constexpr int NQK = KS * KT;  // QK^T MFMAs per sub-tile
+  constexpr int TILE = BK * D;  // elements of one K or V buffer
+  static_assert(NQK == 16 || NQK == 8, "interleave assumes 8 or 16 QK^T MFMAs");
   using Copy = TileCopy<D, BK, NW>;
-  constexpr int NL = Copy::NL;
   // A row moves its reference max only when a sub-tile max exceeds it by
   // more than this many powers of two; until then probabilities are taken
   // against the stale max and stay below 2^8, far from fp32 or bf16 overflow.
@@ -189,6 +207,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
                          half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+    // Retire these loads now: the tile copies below are counted on the same
+    // vector-memory counter and are awaited explicitly.
+    wait_vmcnt<0>();
   }
 
   int nblk;
@@ -242,11 +263,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-  float m_run = -__builtin_inff();  // reference max (log2 units) of this row
   const float sl2 = p.scale_log2;
 
   // LDS element offsets that do not depend on the block.
-  const int sw = swz<CPR>(col);  // swizzle of K rows kt*32 + col
+  const int sw = swz<CPR>(col);  // swizzle of K rows 32 kt + col
   int koffs[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koffs[ks] = col * D + (((2 * ks + half) ^ sw) << 3);
@@ -261,104 +281,97 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       voffs[dt][c2] = row * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
     }
 
-  // S = K Q^T for sub-tile `sub` of the K tile in LDS.
-  auto qk = [&](f32x16 (&sd)[KT], int sub) {
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sd[kt][r] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(Ks + (sub * SUB + kt * 32) * D + koffs[ks]);
-        sd[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sd[kt], 0, 0, 0);
-      }
-    }
-  };
-
-  // Pipeline state (blocks): block n is being finished, block n+1 is next.
-  int j1 = -1, nv1 = 0;  // block n+1
-  int j2 = -1, nv2 = 0;  // block n+2
-  int nv0 = 0;           // block n
-  f32x16 sA[KT], sB[KT];
-
-  if (nblk > 0) {
-    const int j0 = block_of(0);
-    nv0 = nvalid_of(j0);
-    kcopy.issue(kbase + load_of(j0) * p.ks1);
-    vcopy.issue(vbase + load_of(j0) * p.vs1);
-    wait_tiles<NL>(1);  // K[0] landed (V[0] may be in flight)
-    lds_barrier();
-    qk(sA, 0);
-    if (nblk > 1) {
-      j1 = block_of(1);
-      nv1 = nvalid_of(j1);
-    }
-    if constexpr (SPB == 1) {
-      lds_barrier();
-      if (nblk > 1) kcopy.issue(kbase + load_of(j1) * p.ks1);
-    }
-  }
-
-  // One pipeline step on sub-tile `sub` of block n; s_cur holds its S,
-  // s_nxt receives the S of the next sub-tile.
-  auto step = [&](int n, int sub, f32x16 (&s_cur)[KT], f32x16 (&s_nxt)[KT]) {
-    const bool last_sub = sub == SPB - 1;
-    const bool has_next = !last_sub || n + 1 < nblk;
-    if (last_sub && n + 2 < nblk) {
-      j2 = block_of(n + 2);
-      nv2 = nvalid_of(j2);
-    }
-    // Padded keys of this sub-tile get -inf.
-    const int nvs = nv0 - sub * SUB;  // real keys of this sub-tile (may be <= 0)
-    if (nvs < SUB) {
+  // Softmax state of the sub-tile about to be finished.
+  float m_run = -__builtin_inff();  // reference max (log2 units) of this row
+  float m_use = 0.0f, alpha = 1.0f;
+  bool need = false;
+  // Mask, row max and reference update for a freshly computed S (keys of the
+  // sub-tile at or past `nvs` are padding).
+  auto mask = [&](f32x16 (&sd)[KT], int nvs) {
+    if (nvs < SUB) {  // only sub-tiles that hold padding (uniform branch)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (key >= nvs) s_cur[kt][r] = -__builtin_inff();
+          sd[kt][r] = key < nvs ? sd[kt][r] : -__builtin_inff();
         }
     }
-    if (last_sub && has_next) {
-      // K of block n+1 must have landed. With one sub-tile per block it was
-      // issued before V of block n (n = 0) or after it; with two it was
-      // issued in this block's first step and nothing followed it.
-      wait_tiles<NL>((SPB == 1 && n >= 1) ? 1 : 0);
-      lds_barrier();
-    }
-
-    // ---- S of the next sub-tile on the matrix cores || softmax of S[cur].
-    if (has_next) qk(s_nxt, last_sub ? 0 : sub + 1);
+  };
+  auto prep = [&](f32x16 (&sd)[KT]) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2)
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_cur[kt][r], s_cur[kt][r + 1]));
+        mx = __builtin_fmaxf(mx, __builtin_fmaxf(sd[kt][r], sd[kt][r + 1]));
     mx = max_with_other_half(mx) * sl2;
-    const bool need = mx > m_run + kRescaleSlack;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+    need = mx > m_run + kRescaleSlack;
+    const float e_alpha = __builtin_amdgcn_exp2f(m_run - mx);
+    alpha = need ? e_alpha : 1.0f;
     m_run = need ? mx : m_run;
-    const float m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-    bf16x8 pf[2 * KT];
+    m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+  };
+
+  // Block bookkeeping: nv0 = real keys of block n; (j1, nv1) block n+1;
+  // (j2, nv2) block n+2.
+  int nv0 = 0, j1 = -1, nv1 = 0, j2 = -1, nv2 = 0;
+  f32x16 sA[KT], sB[KT];
+
+  if (nblk > 0) {
+    const int j0 = block_of(0);
+    nv0 = nvalid_of(j0);
+    kcopy.issue(kbase + load_of(j0) * p.ks1, 0);
+    vcopy.issue(vbase + load_of(j0) * p.vs1, 0);
+    if (nblk > 1) {
+      j1 = block_of(1);
+      nv1 = nvalid_of(j1);
+      kcopy.issue(kbase + load_of(j1) * p.ks1, TILE * 2);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+      for (int r = 0; r < 16; ++r) sA[kt][r] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[2 * kt + s2][e] =
-              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[kt][8 * s2 + e], sl2, -m_use));
-    if (has_next) {
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int k = 0; k < KS * KT; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+      for (int kt = 0; kt < KT; ++kt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + koffs[ks]);
+        sA[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sA[kt], 0, 0, 0);
       }
-    }
+    mask(sA, nv0);
+    prep(sA);
+  }
 
+  // One pipeline step on sub-tile `sub` of block n. KP / VP are the LDS
+  // buffers read in this step (K of the next sub-tile, V of this one).
+  auto step = [&](auto kp_c, auto vp_c, int n, int sub, f32x16 (&s_cur)[KT],
+                  f32x16 (&s_nxt)[KT]) {
+    constexpr int KP = decltype(kp_c)::value;
+    constexpr int VP = decltype(vp_c)::value;
+    const bool last_sub = sub == SPB - 1;
+    const bool has_next = !last_sub || n + 1 < nblk;
+    if (last_sub) {
+      j2 = (n + 2 < nblk) ? block_of(n + 2) : -1;
+      nv2 = (n + 2 < nblk) ? nvalid_of(j2) : 0;
+    }
+    // ---- the step's single synchronisation point.
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (sub == 0 && n + 1 < nblk) vcopy.issue(vbase + load_of(j1) * p.vs1, (VP ^ 1) * TILE * 2);
+    if (last_sub && n + 2 < nblk) kcopy.issue(kbase + load_of(j2) * p.ks1, (KP ^ 1) * TILE * 2);
+    const uint16_t* kb = Ks + KP * TILE + (last_sub ? 0 : (sub + 1) * SUB * D);
+    const uint16_t* vb = Vs + VP * TILE + sub * SUB * D;
+    if (sub == 0 && nv0 < BK) {
+      // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows.
+      constexpr int NT = NW * 64;
+      uint4* vz = reinterpret_cast<uint4*>(Vs + VP * TILE + nv0 * D);
+      const int nz = (BK - nv0) * D / 8;
+      for (int e = threadIdx.x; e < nz; e += NT) vz[e] = make_uint4(0, 0, 0, 0);
+      lds_barrier();
+    }
     // Lazy rescale of the running output (rare after the first sub-tiles).
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
       lacc[0] *= alpha;
@@ -368,67 +381,87 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
 
-    // The K tile is free once the last sub-tile of the block it holds has
-    // been multiplied: with one sub-tile per block that happened just now for
-    // block n+1 (refill with n+2), with two it happened in the first step of
-    // block n (refill with n+1).
-    if constexpr (SPB == 1) {
-      lds_barrier();
-      if (n + 2 < nblk) kcopy.issue(kbase + load_of(j2) * p.ks1);
-    } else {
-      if (sub == SPB - 2) {
-        lds_barrier();
-        if (n + 1 < nblk) kcopy.issue(kbase + load_of(j1) * p.ks1);
-      }
-    }
-    if (sub == 0) {
-      // V of block n; the K copy issued just above may still be in flight.
-      wait_tiles<NL>((SPB == 1 ? n + 2 < nblk : n + 1 < nblk) ? 1 : 0);
-      lds_barrier();
-      if (nv0 < BK) {
-        // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows.
-        constexpr int NT = NW * 64;
-        uint4* vz = reinterpret_cast<uint4*>(Vs + nv0 * D);
-        const int nz = (BK - nv0) * D / 8;
-        for (int e = threadIdx.x; e < nz; e += NT) vz[e] = make_uint4(0, 0, 0, 0);
-        lds_barrier();
-      }
-    }
-
-    // ---- O^T += V^T P^T. V^T fragment of lane: row d = dt*32 + col,
-    //      k-slots 0..3 / 4..7 = keys base + 0..3 / base + 8 + 0..3 with
-    //      base = 32 kt + 16 s2 + 4 half; one transpose read per group of 4.
+    // ---- (a) S[u+1] = K Q^T || exponentials of P[u] || V^T reads.
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kb = (sub * SUB + kt * 32 + 16 * s2) * D;
-        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[2 * kt + s2], lacc, 0, 0, 0);
+      for (int r = 0; r < 16; ++r) s_nxt[kt][r] = 0.0f;
+    bf16x8 pf[2 * KT];
+    bf16x4 vf[2 * KT][DT][2];
+    constexpr int EXP_PER = (2 * KT * 8) / NQK;   // exponentials per MFMA slot
+    constexpr int VRD_PER = (2 * KT * DT * 2) / NQK;  // V reads per MFMA slot
+    // K fragments are read two MFMA slots ahead of their use.
+    constexpr int KPF = 2;
+    bf16x8 kf[KPF + 1];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const bf16x4 v0 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + kb + voffs[dt][0]));
-          const bf16x4 v1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(Vs + kb + voffs[dt][1]));
-          const bf16x8 a = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[2 * kt + s2], o[dt], 0, 0, 0);
-        }
+    for (int k = 0; k < KPF; ++k)
+      kf[k] = *reinterpret_cast<const bf16x8*>(kb + (k % KT) * 32 * D + koffs[k / KT]);
+#pragma unroll
+    for (int k = 0; k < NQK; ++k) {
+      const int ks = k / KT, kt = k % KT;
+      if (k + KPF < NQK)
+        kf[(k + KPF) % (KPF + 1)] = *reinterpret_cast<const bf16x8*>(
+            kb + ((k + KPF) % KT) * 32 * D + koffs[(k + KPF) / KT]);
+      s_nxt[kt] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % (KPF + 1)], qf[ks], s_nxt[kt], 0, 0, 0);
+#pragma unroll
+      for (int x = 0; x < EXP_PER; ++x) {
+        const int idx = k * EXP_PER + x;           // element of P[u], 0 .. 16 KT - 1
+        const int pk = idx / 8, pe = idx % 8;      // fragment and slot
+        const int skt = pk / 2, sr = 8 * (pk % 2) + pe;
+        pf[pk][pe] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[skt][sr], sl2, -m_use));
       }
+#pragma unroll
+      for (int x = 0; x < VRD_PER; ++x) {
+        const int idx = k * VRD_PER + x;           // 0 .. 4 KT DT - 1
+        const int ks2 = idx / (DT * 2), dt = (idx / 2) % DT, c2 = idx % 2;
+        const int kt2 = ks2 / 2, s2 = ks2 % 2;
+        vf[ks2][dt][c2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4*)(vb + (kt2 * 32 + 16 * s2) * D + voffs[dt][c2]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // With no next sub-tile, S[u+1] is a dummy product and every key of it
+    // counts as padding, which leaves the softmax state unchanged.
+    const int nvs_next = !has_next ? 0 : (last_sub ? nv1 : nv0 - (sub + 1) * SUB);
+    mask(s_nxt, nvs_next);
+    // ---- (b) O += V^T P[u]^T and row sums || row max of S[u+1].
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2 * KT; ++ks2) {
+      lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks2], lacc, 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16x8 av =
+            __builtin_shufflevector(vf[ks2][dt][0], vf[ks2][dt][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks2], o[dt], 0, 0, 0);
+      }
+    }
+    prep(s_nxt);
+
     if (last_sub) {
-      lds_barrier();  // every wave is done with the V tile
-      if (n + 1 < nblk) vcopy.issue(vbase + load_of(j1) * p.vs1);
       nv0 = nv1;
       j1 = j2;
       nv1 = nv2;
     }
   };
 
-  // Sub-tiles in order, two per loop turn so that the S registers alternate
-  // statically between sA and sB.
-  const int nsub = nblk * SPB;
-  for (int u = 0; u < nsub; u += 2) {
-    step(u / SPB, u % SPB, sA, sB);
-    if (u + 1 < nsub) step((u + 1) / SPB, (u + 1) % SPB, sB, sA);
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  // Steps in order, two blocks per loop turn so that the LDS buffers and the
+  // S registers alternate statically.
+  for (int n = 0; n < nblk; n += 2) {
+    if constexpr (SPB == 1) {
+      step(C1{}, C0{}, n, 0, sA, sB);
+      if (n + 1 < nblk) step(C0{}, C1{}, n + 1, 0, sB, sA);
+    } else {
+      step(C0{}, C0{}, n, 0, sA, sB);
+      step(C1{}, C0{}, n, 1, sB, sA);
+      if (n + 1 < nblk) {
+        step(C1{}, C1{}, n + 1, 0, sA, sB);
+        step(C0{}, C1{}, n + 1, 1, sB, sA);
+      }
+    }
   }
 
   // ---- epilogue: O^T lane layout is query col, d = dt*32 + (r/4)*8 + half*4 + r%4.
@@ -453,10 +486,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 }
 
 template <int D, int BQ, int BK, bool DENSE>
-__global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(1, 1)))
 attn_fwd_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * BK * D];
   attn_fwd_body<D, BQ, BK, DENSE>(p, Ks, Vs);
 }
 
