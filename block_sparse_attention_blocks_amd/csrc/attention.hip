@@ -31,6 +31,7 @@
 //    XCD's L2.
 
 #include <type_traits>
+#include <utility>
 
 #include "internal.h"
 
@@ -97,38 +98,36 @@ struct TileCopy {
   static constexpr int RPI = 64 / CPR;
   static constexpr int NL = BK / (NW * RPI);
   static_assert(NL * NW * RPI == BK, "tile split");
-  static_assert((NW * RPI) % 8 == 0, "the swizzle must repeat every two instructions");
-  uint32_t voff[2];     // per-lane byte offset inside the tile, by instruction parity
-  uint32_t step_bytes;  // uniform byte step between two instructions
-  uint32_t lds_base;    // uniform LDS byte address of this wave's first rows
+  uint32_t voff[NL];  // per-lane byte offset of instruction `it` inside the tile
+  uint32_t lds_base;  // uniform LDS byte address of this wave's first rows
 
   __device__ __forceinline__ void init(int64_t row_stride, int wave, int lane, const uint16_t* lds) {
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int row = (par * NW + wave) * RPI + lane / CPR;
+    for (int it = 0; it < NL; ++it) {
+      const int row = (it * NW + wave) * RPI + lane / CPR;
       const int lch = (lane % CPR) ^ swz<CPR>(row);
-      voff[par] = (uint32_t)((row * row_stride + lch * 8) * 2 - par * NW * RPI * row_stride * 2);
+      voff[it] = (uint32_t)((row * row_stride + lch * 8) * 2);
     }
-    step_bytes = (uint32_t)(NW * RPI * row_stride * 2);
     lds_base = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)lds) +
                (uint32_t)(wave * RPI * D * 2);
   }
+  template <int IT>
+  __device__ __forceinline__ void one(const uint16_t* tile, uint32_t lbase) const {
+    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff[IT]), "s"(tile), "s"(lbase), "i"(IT * NW * RPI * D * 2)
+                 : "memory", "m0");
+  }
+  template <int... IT>
+  __device__ __forceinline__ void all(const uint16_t* tile, uint32_t lbase,
+                                      std::integer_sequence<int, IT...>) const {
+    (one<IT>(tile, lbase), ...);
+  }
   // `tile` is the uniform address of row 0 of the tile; `lds_off` selects
-  // the LDS buffer (bytes). The uniform address arithmetic is redone at each
-  // call (the empty asm statements hide the loop-invariant parts from
-  // hoisting), which keeps scalar registers free.
+  // the LDS buffer (bytes). Each copy instruction costs one scalar add (its
+  // LDS destination) besides the copy itself.
   __device__ __forceinline__ void issue(const uint16_t* tile, uint32_t lds_off = 0) const {
-    uint32_t step = step_bytes, lbase = lds_base + lds_off;
-    asm volatile("" : "+s"(step), "+s"(lbase));
-#pragma unroll
-    for (int it = 0; it < NL; ++it) {
-      const char* g = reinterpret_cast<const char*>(tile) + (size_t)(it * step);
-      const uint32_t m0v = lbase + (uint32_t)(it * NW * RPI * D * 2);
-      asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                   :
-                   : "v"(voff[it & 1]), "s"(g), "s"(m0v)
-                   : "memory", "m0");
-    }
+    all(tile, lds_base + lds_off, std::make_integer_sequence<int, NL>{});
   }
 };
 
