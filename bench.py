@@ -1,12 +1,15 @@
 """Benchmark: selected-block attention at 75 % sparsity on the 48k-token
 edge-video-shaped workload, one MI355X.
 
-One step = the whole hot path over one synthetic input set already in HBM:
-block selection (pooling + scores + top-k) followed by block-sparse
-attention. Prints one JSON line. ``value`` is effective attention TFLOP/s of
-the step (4 * block_q * block_k * head_dim FLOP per selected tile, selection
-time included in the denominator); the attention kernel alone is reported in
-``roofline`` against the bf16 MFMA peak.
+One step = the whole hot path over synthetic inputs already in HBM: block
+selection (pooling + scores + top-k) followed by block-sparse attention
+(``edge48k``, ``video720p``); dense attention alone (``dense8k``); or the
+36-layer two-stream schedule, 8 dense layers then 28 selected-sparse layers
+(``twostream``). Prints one JSON line. ``value`` is effective attention
+TFLOP/s of the step (4 * block_q * block_k * head_dim FLOP per selected tile,
+selection time included in the denominator); the attention kernel alone is
+reported in ``roofline`` against the bf16 MFMA peak, timed with HIP events on
+the stream the kernels are launched on.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload edge48k]
                        [--no-cpu-baseline]
@@ -27,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 4096 FLOP/clk x 2.4 GHz)
 ATTN_KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_blocks_amd", "csrc", "attention.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_edge48k_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_TEXT = {
     "edge48k": ("edge-video-shaped sparse attention: batch 1, 32 query / 8 KV heads, head_dim 128, "
@@ -35,7 +38,11 @@ WORKLOAD_TEXT = {
                 "64x64 blocks, 75% target sparsity (191 of 764 KV blocks per row)"),
     "dense8k": "dense GQA: batch 1, 32 query / 8 KV heads, head_dim 128, 8,192 tokens, 128x128 blocks",
     "video720p": ("720p-video-shaped sparse attention: 32/8 heads, head_dim 128, 512 prefix + "
-                  "172,800 generation tokens, 128x128 blocks, 75% target"),
+                  "172,800 generation tokens (48x45x80), 128x128 blocks, 75% target (339 of 1354)"),
+    "twostream": ("two-stream schedule: generation stream of 20,000 tokens (padded to 20,096) "
+                  "attending to cat(understanding stream of 1,000 tokens padded to 1,024, "
+                  "generation stream), 32/8 heads, head_dim 128, 128x128 blocks, 36 layers with "
+                  "fresh inputs: 8 dense, then 28 at 75% target (42 of 165 blocks)"),
 }
 
 
@@ -45,7 +52,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="edge48k", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--input-sets", type=int, default=3)
+    ap.add_argument("--input-sets", type=int, default=3,
+                    help="distinct input sets rotated over the steps (twostream: always its 36 layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-blocks", type=int, default=756)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -59,13 +67,15 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def recorded_traffic():
+def recorded_traffic(name):
     """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    summary of this workload, if it was taken on the current kernel source;
+    else None."""
+    path = os.path.join(PROFILES, f"attn_fwd_{name}_traffic.txt")
+    if not os.path.exists(path):
         return None
     vals = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -80,9 +90,10 @@ def recorded_traffic():
 
 def cpu_baseline(case, keep, n_blocks):
     """The fp64 oracle, untouched, on a bounded sample of the same workload:
-    selection for query head 0 (all its query blocks) and attention for the
-    first ``n_blocks`` query blocks of that head. Reported as effective
-    TFLOP/s of the sampled blocks, the selection time pro-rated to them."""
+    selection for query head 0 (all its query blocks; skipped for a dense
+    layer, ``keep`` None) and attention for the first ``n_blocks`` query
+    blocks of that head. Reported as effective TFLOP/s of the sampled blocks,
+    the selection time pro-rated to them."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -94,8 +105,11 @@ def cpu_baseline(case, keep, n_blocks):
     k1 = np.ascontiguousarray(case.k[:, :, g:g + 1])
     v1 = np.ascontiguousarray(case.v[:, :, g:g + 1])
     t0 = time.perf_counter()
-    idx, cnt = oracle.select(lay1, q1, k1, keep)
-    t_sel = time.perf_counter() - t0
+    if keep is None:
+        idx, cnt = oracle.identity_selection(lay1)
+    else:
+        idx, cnt = oracle.select(lay1, q1, k1, keep)
+    t_sel = time.perf_counter() - t0 if keep is not None else 0.0
     nq = lay["q_len"] // lay["block_q"]
     n_blocks = min(n_blocks, nq)
     idx_s = idx[:, :, :n_blocks]
@@ -107,11 +121,13 @@ def cpu_baseline(case, keep, n_blocks):
     flops = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * float(cnt_s.sum())
     t = t_sel * n_blocks / nq + t_att
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    what = "dense (no selection)" if keep is None else f"selection over all {nq} query blocks " \
+        f"({t_sel:.2f} s, pro-rated)"
     return {
         "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"query head 0 of {hq}: selection over all {nq} query blocks "
-                   f"({t_sel:.2f} s, pro-rated) + fp64 attention for {n_blocks} query blocks "
-                   f"({t_att:.2f} s); effective FLOPs of those blocks"),
+        "sample": (f"{case.name} layer {case.meta.get('layer', 0)}, query head 0 of {hq}: {what}"
+                   f" + fp64 attention for {n_blocks} query blocks ({t_att:.2f} s); effective "
+                   "FLOPs of those blocks"),
         "seconds": round(t_sel + t_att, 2),
     }
 
@@ -131,8 +147,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = args.workload
+    schedule = name == "twostream"
+    n_sets = synth.CONFIGS[name]["layers"] if schedule else max(1, args.input_sets)
     sets = []
-    for layer in range(max(1, args.input_sets)):
+    for layer in range(n_sets):
         case = synth.make_config(name, layer=layer)
         t = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
              for a in (case.q, case.k, case.v)]
@@ -141,25 +159,40 @@ def main():
     case0 = sets[0][0]
     lay = case0.layout
     nq, nk, p = bsa.num_blocks(lay)
-    keep = bsa.keep_blocks(nk, p, case0.sparsity)
     b, hq = lay["batch"], lay["num_q_heads"]
+    sparse_case = next((c for c, _ in sets if c.sparsity > 0), None)
+    keep = bsa.keep_blocks(nk, p, sparse_case.sparsity) if sparse_case else nk
     idx = torch.empty((b, hq, nq, keep), dtype=torch.int32, device=dev)
     cnt = torch.empty((b, hq, nq), dtype=torch.int32, device=dev)
     ws = torch.empty(max(bsa.select_workspace_size(lay), 256), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(t[0]) for _, t in sets]
     stream = torch.cuda.current_stream()
 
-    def step(s, ev=None):
+    # One step: a list of (input set, dense?) layer calls.
+    if schedule:
+        plan = [[(s, sets[s][0].sparsity == 0) for s in range(len(sets))]]
+    else:
+        plan = [[(s, case0.sparsity == 0)] for s in range(len(sets))]
+
+    def layer_call(s, dense, ev=None):
         _, (q, k, v) = sets[s]
         if ev is not None:
             ev[0].record(stream)
-        bsa.select_blocks(q, k, lay, keep, keep, block_idx=idx, block_cnt=cnt, workspace=ws,
-                          stream=stream)
+        if not dense:
+            bsa.select_blocks(q, k, lay, keep, keep, block_idx=idx, block_cnt=cnt, workspace=ws,
+                              stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        bsa.block_sparse_attention(q, k, v, idx, cnt, lay, out=outs[s], stream=stream)
+        if dense:
+            bsa.dense_attention(q, k, v, lay, out=outs[s], stream=stream)
+        else:
+            bsa.block_sparse_attention(q, k, v, idx, cnt, lay, out=outs[s], stream=stream)
         if ev is not None:
             ev[2].record(stream)
+
+    def step(i, evs=None):
+        for j, (s, dense) in enumerate(plan[i % len(plan)]):
+            layer_call(s, dense, None if evs is None else evs[j])
 
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
@@ -168,32 +201,50 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Warm up every layout (each input set) before timing.
-    for w in range(max(args.warmup, len(sets))):
-        step(w % len(sets))
-    torch.cuda.synchronize()
-    # Expected sparse dispatch: every real query block keeps exactly `keep` blocks.
+    # Warm up every layout (each input set) before timing; count the effective
+    # work of each step from the counts the selector actually produced.
+    tile_flops = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"]
     real_rows = (torch.arange(nq, device=dev) * lay["block_q"] < lay["q_valid"])
-    if not bool((cnt[:, :, real_rows] == keep).all()):
-        raise RuntimeError("unexpected block counts after selection")
-    selected_tiles = float(cnt.sum().item())
-    eff_flops = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * selected_tiles
+    step_flops = []
+    for i in range(len(plan)):
+        f = 0.0
+        for s, dense in plan[i]:
+            layer_call(s, dense)
+            if dense:
+                f += tile_flops * b * hq * nq * nk
+            else:
+                torch.cuda.synchronize()
+                if not bool((cnt[:, :, real_rows] == keep).all()):
+                    raise RuntimeError("unexpected block counts after selection")
+                f += tile_flops * float(cnt.sum().item())
+        step_flops.append(f)
+    for w in range(args.warmup):
+        step(w)
+    torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    n_calls = len(plan[0])
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_calls)]
+              for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(s % len(sets), events[s])
+    for i in range(args.steps):
+        step(i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sel_ms = [e[0].elapsed_time(e[1]) for e in events]
-    att_ms = [e[1].elapsed_time(e[2]) for e in events]
+    sel_ms = [sum(e[0].elapsed_time(e[1]) for e in ev) for ev in events]
+    att_ms = [sum(e[1].elapsed_time(e[2]) for e in ev) for ev in events]
+    eff_flops = float(np.mean([step_flops[i % len(plan)] for i in range(args.steps)]))
     ms_per_step = wall * 1e3 / args.steps
     att_avg = float(np.mean(att_ms))
     att_tflops = eff_flops / (att_avg * 1e-3) / 1e12
     value = eff_flops / (ms_per_step * 1e-3) / 1e12
 
-    traffic = recorded_traffic()
+    dense_only = all(d for call in plan for _, d in call)
+    kname = f"attn_fwd_kernel<{lay['head_dim']},{lay['block_q']},{lay['block_k']}," \
+        f"{'dense' if dense_only else 'sparse'}>"
+    if schedule:
+        kname += " (8 dense + 28 sparse launches per step)"
+    traffic = recorded_traffic(name)
     result = {
         "metric": "effective attention TFLOP/s + ms/call at 75% sparsity, 48k tokens, 1 MI355X",
         "value": round(value, 2),
@@ -211,15 +262,17 @@ def main():
                    "q_heads": hq, "kv_heads": lay["num_kv_heads"], "head_dim": lay["head_dim"],
                    "q_len": lay["q_len"], "kv_len": lay["kv_len"],
                    "block": f"{lay['block_q']}x{lay['block_k']}", "kv_blocks": nk,
-                   "kept_blocks": keep, "sparsity_pct": case0.sparsity,
-                   "input_sets": len(sets)},
-        "attn_ms_per_call": round(att_avg, 4),
-        "attn_ms_min": round(float(np.min(att_ms)), 4),
+                   "kept_blocks": keep, "sparsity_pct": sparse_case.sparsity if sparse_case else 0,
+                   "input_sets": len(sets), "calls_per_step": n_calls},
+        "attn_ms_per_call": round(att_avg / n_calls, 4),
+        "attn_ms_per_step": round(att_avg, 4),
+        "attn_ms_median": round(float(np.median(att_ms)) / n_calls, 4),
+        "attn_ms_min": round(float(np.min(att_ms)) / n_calls, 4),
         "attn_tflops": round(att_tflops, 2),
-        "select_ms_per_call": round(float(np.mean(sel_ms)), 4),
-        "effective_tflop_per_call": round(eff_flops / 1e12, 4),
+        "select_ms_per_step": round(float(np.mean(sel_ms)), 4),
+        "effective_tflop_per_step": round(eff_flops / 1e12, 4),
         "roofline": {
-            "kernel": "attn_fwd_kernel<128,64,64,sparse>",
+            "kernel": kname,
             "bound": "mfma",
             "achieved": round(att_tflops, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -230,7 +283,9 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case0, keep, args.cpu_sample_blocks)
+        cb_case = sparse_case if sparse_case is not None else case0
+        result["cpu_baseline"] = cpu_baseline(cb_case, keep if sparse_case is not None else None,
+                                              args.cpu_sample_blocks)
     print(json.dumps(result), flush=True)
 
 

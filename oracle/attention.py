@@ -96,35 +96,54 @@ def attend(layout: dict, q_bits, k_bits, v_bits, idx, cnt):
 
 
 def attend_rows(layout: dict, q_bits, k_bits, v_bits, idx, cnt, rows):
-    """Oracle attention for chosen query rows only.
+    """Oracle attention for chosen query rows only (the full-size checks).
 
     ``rows`` [B, Hq, R] query-row indices. Returns o [B, Hq, R, D] and
-    lse [B, Hq, R]."""
+    lse [B, Hq, R].
+
+    Same definition as ``attend``: for row t of query block i, softmax over
+    the valid keys of the blocks listed for (b, h, i). Evaluated for all R
+    rows of a head at once: logits against every key of KV head h // G, then
+    every key outside a row's selected valid set gets weight exactly 0 (its
+    logit never enters the max, its value row is replaced by 0 so that
+    nothing it holds can reach the sum).
+    """
     hq, hkv = layout["num_q_heads"], layout["num_kv_heads"]
     grp = hq // hkv
-    bq = layout["block_q"]
+    bq, bk = layout["block_q"], layout["block_k"]
     scale = _scale(layout)
     kmask, qmask = valid_key_mask(layout), valid_query_mask(layout)
     b_, _, _, d = q_bits.shape
+    lk = k_bits.shape[1]
+    n_k = lk // bk
     nr = rows.shape[2]
     o = np.zeros((b_, hq, nr, d))
     lse = np.full((b_, hq, nr), -np.inf)
     for b in range(b_):
-        for h in range(hq):
-            g = h // grp
-            for r in range(nr):
-                t = int(rows[b, h, r])
-                if not qmask[t]:
+        for g in range(hkv):
+            kg = widen_bf16(k_bits[b, :, g, :])
+            vg = np.where(kmask[:, None], widen_bf16(v_bits[b, :, g, :]), 0.0)
+            for h in range(g * grp, (g + 1) * grp):
+                t = rows[b, h].astype(np.int64)
+                keys = np.zeros((nr, n_k), dtype=bool)
+                for r in range(nr):
+                    if not qmask[t[r]]:
+                        continue
+                    i = t[r] // bq
+                    c = int(cnt[b, h, i])
+                    keys[r, np.asarray(idx[b, h, i, :c], dtype=np.int64)] = True
+                keys = np.repeat(keys, bk, axis=1) & kmask[None, :]
+                live = keys.any(axis=1)
+                if not live.any():
                     continue
-                i = t // bq
-                u = _selected_keys(layout, kmask, idx[b, h, i], int(cnt[b, h, i]))
-                if u.size == 0:
-                    continue
-                qt = widen_bf16(q_bits[b, t, h, :])[None, :]
-                ob, lb = _softmax_rows(qt, widen_bf16(k_bits[b, u, g, :]),
-                                       widen_bf16(v_bits[b, u, g, :]), scale)
-                o[b, h, r] = ob[0]
-                lse[b, h, r] = lb[0]
+                qr = widen_bf16(q_bits[b, t[live], h, :])
+                sel = keys[live]
+                logits = np.where(sel, scale * (qr @ kg.T), -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                p = np.where(sel, np.exp(logits - m), 0.0)
+                l = p.sum(axis=1, keepdims=True)
+                o[b, h, live] = (p @ vg) / l
+                lse[b, h, live] = (m + np.log(l))[:, 0]
     return o, lse
 
 

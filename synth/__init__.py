@@ -18,14 +18,17 @@ patterns, C-contiguous):
   ``cosmos_parallel.py``, ``shard_cosmos3_sequence``).
 
 Values: fp64 draws, rounded to fp32 and then to bf16 (round to nearest even
-at each step). Seeds are ``SeedSequence([42, cfg, layer, stream])`` with
-stream 0 = Q, 1 = K, 2 = V, 3 = structure, 4 = row sampling; 42 is the
+at each step). Seeds are ``SeedSequence([42, cfg, layer, stream, ...])`` with
+stream 0 = Q, 1 = K, 2 = V, 3 = structure, 4 = row sampling (Q/K/V rows add
+batch row, segment and a 2048-row chunk number to the key); 42 is the
 generation seed the Cosmos3-Nano and MiniMax H3 measurements used (vllm-omni
 PR #8583 "Test Result"; PR #8644 "Test Plan").
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -99,24 +102,45 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def _normal_rows(rng, rows, heads, d, chunk=4096):
-    """[rows, heads, d] i.i.d. N(0,1) fp64, drawn in fixed-size row chunks."""
+CHUNK_ROWS = 2048
+
+
+def _chunk_rng(key, chunk: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED, *key, chunk])))
+
+
+def _gen_rows(key, rows, heads, d, add=None):
+    """[rows, heads, d] bf16 bits of i.i.d. N(0,1) fp64 draws (+ ``add(t0, t1)``).
+
+    Rows are drawn in chunks of CHUNK_ROWS; chunk c draws from its own
+    generator seeded with ``SeedSequence([42, *key, c])``, so the chunks are
+    independent of each other and are filled on a thread pool (numpy releases
+    the GIL in bulk draws and ufuncs). The bytes do not depend on the number
+    of threads."""
     out = np.empty((rows, heads, d), dtype=np.uint16)
-    for r0 in range(0, rows, chunk):
-        r1 = min(rows, r0 + chunk)
-        out[r0:r1] = to_bf16_bits(rng.standard_normal((r1 - r0, heads, d)))
+
+    def fill(c):
+        r0, r1 = c * CHUNK_ROWS, min(rows, (c + 1) * CHUNK_ROWS)
+        z = _chunk_rng(key, c).standard_normal((r1 - r0, heads, d))
+        if add is not None:
+            z += add(r0, r1)
+        out[r0:r1] = to_bf16_bits(z)
+
+    n = (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+    if n <= 1:
+        for c in range(n):
+            fill(c)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=min(n, _threads())) as ex:
+            list(ex.map(fill, range(n)))
     return out
 
 
-def _gen_rows(rng, rows, heads, d, add=None, chunk=4096):
-    """Like ``_normal_rows`` (same draws), plus ``add(t0, t1)`` per chunk if given."""
-    if add is None:
-        return _normal_rows(rng, rows, heads, d, chunk)
-    out = np.empty((rows, heads, d), dtype=np.uint16)
-    for r0 in range(0, rows, chunk):
-        r1 = min(rows, r0 + chunk)
-        out[r0:r1] = to_bf16_bits(rng.standard_normal((r1 - r0, heads, d)) + add(r0, r1))
-    return out
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:
+        return max(1, min(16, os.cpu_count() or 1))
 
 
 def _lowrank_structure(cfg, layer, frames, hq, hkv, d, rank=8):
@@ -207,13 +231,17 @@ def make_case(name="custom", *, cfg=0, layer=0, batch=1, hq=2, hkv=1, d=64, bq=6
                     return 2.0 * np.einsum("nhr,hrd->nhd", rc, ub)
                 basis = st["u"] if which == "k" else st["w"]
                 return 2.0 * np.einsum("nr,grd->ngd", c, basis)
-        rq, rk, rv = (rng_for(cfg, layer, s) for s in (STREAM_Q, STREAM_K, STREAM_V))
         for bi in range(batch):
-            q[bi, :gen] = _gen_rows(rq, gen, hq, d, add and (lambda a, b: add("q", a, b)))
-            k[bi, :prefix] = _normal_rows(rk, prefix, hkv, d)
-            k[bi, pl:pl + gen] = _gen_rows(rk, gen, hkv, d, add and (lambda a, b: add("k", a, b)))
-            v[bi, :prefix] = _normal_rows(rv, prefix, hkv, d)
-            v[bi, pl:pl + gen] = _gen_rows(rv, gen, hkv, d, add and (lambda a, b: add("v", a, b)))
+            # key = (cfg, layer, stream, batch row, segment): segment 0 = generation
+            # tokens, 1 = prefix tokens
+            gk = lambda stream, seg: (cfg, layer, stream, bi, seg)
+            q[bi, :gen] = _gen_rows(gk(STREAM_Q, 0), gen, hq, d, add and (lambda a, b: add("q", a, b)))
+            k[bi, :prefix] = _gen_rows(gk(STREAM_K, 1), prefix, hkv, d)
+            k[bi, pl:pl + gen] = _gen_rows(gk(STREAM_K, 0), gen, hkv, d,
+                                           add and (lambda a, b: add("k", a, b)))
+            v[bi, :prefix] = _gen_rows(gk(STREAM_V, 1), prefix, hkv, d)
+            v[bi, pl:pl + gen] = _gen_rows(gk(STREAM_V, 0), gen, hkv, d,
+                                           add and (lambda a, b: add("v", a, b)))
     elif dist == "int":
         r = rng_for(cfg, layer, STREAM_Q)
         q[:, :gen] = to_bf16_bits(r.integers(-int_range, int_range + 1, size=(batch, gen, hq, d)))

@@ -177,18 +177,22 @@ def test_padding_invariance_and_unpadded_equivalence(fill):
     assert np.abs(o1[0, :300] - ref.permute(1, 0, 2).numpy()).max() < 1e-12
 
 
-def test_attend_rows_matches_attend():
-    case = synth.make_case(hq=4, hkv=2, d=64, prefix=64, gen=400, cfg=30)
+@pytest.mark.parametrize("fill", [None, float("nan")])
+def test_attend_rows_matches_attend(fill):
+    case = synth.make_case(hq=4, hkv=2, d=64, prefix=50, gen=400, cfg=30, pad_fill=fill)
     lay = case.layout
     idx, cnt = oracle.select(lay, case.q, case.k, 4)
     o, lse = oracle.attend(lay, case.q, case.k, case.v, idx, cnt)
     rows = synth.sample_rows(case, 12)
+    rows[..., -1] = lay["q_len"] - 1  # a padded query row
     orow, lrow = oracle.attend_rows(lay, case.q, case.k, case.v, idx, cnt, rows)
+    assert lay["q_valid"] < lay["q_len"]
     for h in range(4):
         for r in range(12):
             t = rows[0, h, r]
             assert np.abs(orow[0, h, r] - o[0, t, h]).max() < 1e-13
-            assert abs(lrow[0, h, r] - lse[0, h, t]) < 1e-13
+            assert lrow[0, h, r] == lse[0, h, t] or abs(lrow[0, h, r] - lse[0, h, t]) < 1e-13
+    assert (orow[0, :, -1] == 0).all() and np.isneginf(lrow[0, :, -1]).all()
 
 
 def test_scale_default_is_inverse_sqrt_head_dim():
