@@ -9,23 +9,34 @@
 // reading KV head h / G in place. The dense case is the same kernel with the
 // list "every non-empty block" generated in-kernel.
 //
-// Structure (one workgroup per query block, one wave per 32 query rows):
-//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K tile (A operand) comes
-//    from LDS, Q^T (B operand) stays in registers for the whole row block.
-//    Each lane then owns one query row (lane % 32) and half of the tile's
-//    keys, so the row max / row sum need a single cross-lane step.
-//  * Online softmax in fp32, exp2 with the scale folded into one FMA.
+// Structure: one workgroup of four waves per 64 query rows (a 128-row query
+// block is two workgroups reading the same list). The keys are streamed in
+// stages of 64; wave (qh, kh) computes query rows [32 qh, 32 qh + 32) against
+// keys [32 kh, 32 kh + 32) of every stage, so both waves of a key half read
+// the same K and V rows from LDS. Each wave keeps its own partial softmax
+// state; the two key halves are merged once at the end. A wave needs fewer
+// than 256 registers, so two workgroups share a CU and every SIMD runs two
+// waves: while one wave waits (LDS, barrier, the HBM copies) the other
+// issues, and one wave's softmax overlaps the other's matrix products.
+//  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K fragment (A operand)
+//    comes from LDS, Q^T (B operand) stays in registers for the whole
+//    kernel. Each lane owns one query row and half of the 32 keys, so the
+//    row max needs a single cross-lane step.
+//  * Online softmax in fp32 in the log2 domain, the scale folded into one
+//    FMA; the reference max of a row moves only when a stage max exceeds it
+//    by more than 2^8 (lazy rescale), and the cross-lane step is skipped when
+//    no lane comes near that. Row sums are accumulated on the vector ALU.
 //  * O^T = V^T P^T with the same MFMA: P^T is the S^T accumulator converted
 //    to bf16 in place (the contraction over keys is order-free, so the key
-//    order of the accumulator layout is reused for V); V^T fragments are
-//    read from the row-major V tile with ds_read_b64_tr_b16. The output
-//    accumulator again has one query per lane, so the softmax rescale is a
-//    per-lane multiply.
-//  * K and V tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging), XOR-swizzled in 16-byte chunks so the K row reads and the
-//    V transpose reads hit distinct banks. K of the next block loads while
-//    this block's softmax and PV run; V of the next block loads while the
-//    next QK^T and softmax run.
+//    order of the accumulator layout is reused for V); V^T fragments come
+//    from the row-major V tile through ds_read_b64_tr_b16.
+//  * Inside a wave the QK^T MFMAs of the next stage are interleaved with the
+//    exponentials of the current one, and the PV MFMAs with the row maxima
+//    of the next.
+//  * K and V stages move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
+//    staging), XOR-swizzled in 16-byte chunks so that the K row reads and
+//    the V transpose reads hit distinct banks, double buffered: K two stages
+//    ahead, V one. One workgroup barrier per stage.
 //  * Workgroups are renumbered so that each XCD works through a contiguous
 //    range of (KV head, query block), keeping that range's K/V tiles in the
 //    XCD's L2.
@@ -51,7 +62,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 //  * the V transpose reads (32 lanes = 4 consecutive rows x 4 adjacent
 //    chunks) 16 distinct chunk positions.
 // With 8 chunks per row two rows share a 256-byte line, and (r / 2) % 8
-// keeps the K reads conflict-free.
+// keeps the K reads conflict-free. Both depend on r % 16 only.
 template <int CPR>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (CPR == 16) {
@@ -80,54 +91,52 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// HBM->LDS copy of one [BK x D] bf16 tile with global_load_lds_dwordx4 in its
-// scalar-base form: the LDS destination comes from M0 and the HBM address is
-// a 64-bit scalar base plus a 32-bit per-lane offset, so issuing a copy costs
-// no vector ALU work. Each wave instruction moves 64 x 16 bytes = RPI whole
-// rows; instruction `it` of wave `wave` fills rows (it * NW + wave) * RPI +
-// [0, RPI). The row step between instructions is a multiple of 8 rows, so the
-// XOR swizzle of a lane's chunk is the same for every instruction and the
-// per-lane offset is fixed for the whole kernel.
+// HBM->LDS copy of this wave's 16 rows (rows 16 w .. 16 w + 15) of a 64-row
+// stage, with global_load_lds_dwordx4 in its scalar-base form: the LDS
+// destination comes from M0 and the HBM address is a 64-bit scalar base plus
+// a 32-bit per-lane offset, so a copy costs no vector ALU work. Instruction
+// `it` moves 64 x 16 bytes = RPI whole rows. The lane's chunk within its row
+// carries the XOR swizzle, which depends on the row modulo 16 only.
 //
 // The copies are issued from inline assembly, so the compiler does not track
-// them: every read of a tile is preceded by an explicit wait_vmcnt on the
-// copies that must have landed and an LDS barrier.
-template <int D, int BK, int NW>
-struct TileCopy {
+// them: every read of a stage is preceded by an explicit wait_vmcnt and a
+// workgroup barrier.
+template <int D>
+struct StageCopy {
   static constexpr int CPR = D / 8;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int NL = BK / (NW * RPI);
-  static_assert(NL * NW * RPI == BK, "tile split");
-  uint32_t voff[NL];  // per-lane byte offset of instruction `it` inside the tile
-  uint32_t lds_base;  // uniform LDS byte address of this wave's first rows
+  static constexpr int NL = 16 / RPI;  // instructions per wave and stage
+  uint32_t voff[NL];                   // per-lane byte offsets
 
-  __device__ __forceinline__ void init(int64_t row_stride, int wave, int lane, const uint16_t* lds) {
+  __device__ __forceinline__ void init(int64_t row_stride, int lane) {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
-      const int row = (it * NW + wave) * RPI + lane / CPR;
+      const int row = it * RPI + lane / CPR;
       const int lch = (lane % CPR) ^ swz<CPR>(row);
       voff[it] = (uint32_t)((row * row_stride + lch * 8) * 2);
     }
-    lds_base = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)lds) +
-               (uint32_t)(wave * RPI * D * 2);
   }
   template <int IT>
-  __device__ __forceinline__ void one(const uint16_t* tile, uint32_t lbase) const {
+  __device__ __forceinline__ void one(const uint16_t* rows, uint32_t lds) const {
     asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff[IT]), "s"(tile), "s"(lbase), "i"(IT * NW * RPI * D * 2)
+                 : "v"(voff[IT]), "s"(rows), "s"(lds), "i"(IT * 1024)
                  : "memory", "m0");
   }
-  template <int... IT>
-  __device__ __forceinline__ void all(const uint16_t* tile, uint32_t lbase,
-                                      std::integer_sequence<int, IT...>) const {
-    (one<IT>(tile, lbase), ...);
+  // `rows`: uniform address of this wave's first row; `lds`: LDS byte address
+  // of this wave's part of the stage. `it` is a constant after unrolling.
+  __device__ __forceinline__ void issue_one(int it, const uint16_t* rows, uint32_t lds) const {
+    switch (it) {
+      case 0: one<0>(rows, lds); break;
+      case 1: one<1 % NL>(rows, lds); break;
+      case 2: one<2 % NL>(rows, lds); break;
+      case 3: one<3 % NL>(rows, lds); break;
+      default: break;
+    }
   }
-  // `tile` is the uniform address of row 0 of the tile; `lds_off` selects
-  // the LDS buffer (bytes). Each copy instruction costs one scalar add (its
-  // LDS destination) besides the copy itself.
-  __device__ __forceinline__ void issue(const uint16_t* tile, uint32_t lds_off = 0) const {
-    all(tile, lds_base + lds_off, std::make_integer_sequence<int, NL>{});
+  __device__ __forceinline__ void issue(const uint16_t* rows, uint32_t lds) const {
+#pragma unroll
+    for (int it = 0; it < NL; ++it) issue_one(it, rows, lds);
   }
 };
 
@@ -139,74 +148,69 @@ __device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
   return v;
 }
 
-// Value of the other half-wave: lanes l and l ^ 32 hold the same query row.
+// Lanes l and l ^ 32 hold the same query row (different keys).
 __device__ __forceinline__ float max_with_other_half(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
   return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+__device__ __forceinline__ float sum_with_other_half(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-// Kernel body. One wave per 32 query rows; the keys of each listed KV block
-// are processed as sub-tiles of 64 keys. K and V tiles are double-buffered in
-// LDS and each step starts with the only workgroup barrier of the step: the
-// copies issued one step earlier have landed and the buffers read in the
-// previous step are free for the next copies. Per sub-tile u a wave then runs
-//   (a) S[u+1] = K Q^T on the matrix cores, interleaved instruction by
-//       instruction with the exponentials of P[u] (the row maxima of S[u]
-//       are already known) and the V transpose reads for step (b);
-//   (b) O += V^T P[u]^T and the row sums of P[u] on the matrix cores,
-//       interleaved with the masking and row maxima of S[u+1].
-// One wave per SIMD: the matrix cores and the vector ALUs are kept busy by
-// the interleaving inside the wave rather than by switching waves.
-template <int D, int BQ, int BK, bool DENSE>
-__device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ Ks,
-                                              uint16_t* __restrict__ Vs) {
-  constexpr int NW = BQ / 32;
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, int BK, bool DENSE>
+__device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ smem) {
   constexpr int CPR = D / 8;
-  constexpr int KS = D / 16;    // MFMA k-steps over D
-  constexpr int DT = D / 32;    // output 32-row tiles over D
-  constexpr int SUB = 64;       // keys per pipeline sub-tile
-  constexpr int KT = SUB / 32;  // 32-key MFMA tiles per sub-tile
-  constexpr int SPB = BK / SUB; // sub-tiles per KV block
-  constexpr int NQK = KS * KT;  // QK^T MFMAs per sub-tile
-  constexpr int TILE = BK * D;  // elements of one K or V buffer
-  static_assert(NQK == 16 || NQK == 8, "interleave assumes 8 or 16 QK^T MFMAs");
-  using Copy = TileCopy<D, BK, NW>;
-  // A row moves its reference max only when a sub-tile max exceeds it by
-  // more than this many powers of two; until then probabilities are taken
-  // against the stale max and stay below 2^8, far from fp32 or bf16 overflow.
+  constexpr int KS = D / 16;     // MFMA k-steps over D (QK^T MFMAs per stage)
+  constexpr int DT = D / 32;     // output 32-row tiles over D
+  constexpr int SPB = BK / 64;   // 64-key stages per block
+  constexpr int STAGE = 64 * D;  // elements of one K or V stage
+  static_assert(SPB == 1 || SPB == 2, "block_k 64 or 128");
+  using Copy = StageCopy<D>;
+  // A row moves its reference max only when a stage max exceeds it by more
+  // than this many powers of two; until then probabilities are taken against
+  // the stale max and stay below 2^8, far from fp32 or bf16 overflow.
   constexpr float kRescaleSlack = 8.0f;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qh = wave >> 1;  // query half
+  const int kh = wave & 1;   // key half of every stage
   const int col = lane & 31;
   const int half = lane >> 5;
 
   // Workgroup w runs on XCD w % 8; give each XCD a contiguous range of the
-  // (batch, KV head, query block, head-in-group) order.
+  // (batch, KV head, query block, head-in-group, 64-row part) order.
   const int nwg = p.n_wg;
   const int w = blockIdx.x;
   const int xcd = w & 7, per = nwg >> 3, rem = nwg & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
-  const int hig = lin % p.group;
-  int t = lin / p.group;
+  const int part = lin % p.qparts;
+  int t = lin / p.qparts;
+  const int hig = t % p.group;
+  t /= p.group;
   const int i = t % p.nq;
   t /= p.nq;
   const int g = t % p.hkv;
   const int b = t / p.hkv;
   const int h = g * p.group + hig;
+  const int row0 = i * (64 * p.qparts) + part * 64;
+  const int qrow = row0 + 32 * qh + col;
 
-  const int row0 = i * BQ;
-  const int qrow = row0 + wave * 32 + col;
-
-  // Q^T fragments (B operand): lane holds q[qrow][16 ks + 8 half .. +7].
+  // Q^T fragments (B operand): the lane holds q[qrow][16 ks + 8 half .. +7].
   bf16x8 qf[KS];
   {
-    const uint16_t* qp = p.q + (int64_t)b * p.qs0 + (int64_t)qrow * p.qs1 + (int64_t)h * p.qs2 +
-                         half * 8;
+    const uint16_t* qp =
+        p.q + (int64_t)b * p.qs0 + (int64_t)qrow * p.qs1 + (int64_t)h * p.qs2 + half * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-    // Retire these loads now: the tile copies below are counted on the same
+    // Retire these loads now: the stage copies are counted on the same
     // vector-memory counter and are awaited explicitly.
     wait_vmcnt<0>();
   }
@@ -221,12 +225,19 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     idx_row = p.idx + row_id * p.idx_row_stride;
   }
   if (row0 >= p.q_valid || p.nk == 0) nblk = 0;
+  const int nst = nblk * SPB;  // stages
 
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
   Copy kcopy, vcopy;
-  kcopy.init(p.ks1, wave, lane, Ks);
-  vcopy.init(p.vs1, wave, lane, Vs);
+  kcopy.init(p.ks1, lane);
+  vcopy.init(p.vs1, lane);
+  // LDS: K stages 0, 1 then V stages 0, 1; this wave copies rows 16 wave ..
+  const uint32_t smem_addr =
+      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)smem);
+  const uint32_t wcopy = (uint32_t)(wave * 16 * D * 2);
+  auto k_stage = [&](int s) { return smem_addr + (uint32_t)(s * STAGE * 2) + wcopy; };
+  auto v_stage = [&](int s) { return smem_addr + (uint32_t)((2 + s) * STAGE * 2) + wcopy; };
 
   // Listed block n. Entries outside [0, NK) are copied from block 0 (always
   // in bounds) with no real key, which gives them zero weight.
@@ -246,29 +257,25 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
         (s0 < p.kv_prefix_len) ? p.kv_prefix_valid : p.kv_prefix_len + p.kv_suffix_valid;
     return min(max(seg_end - s0, 0), BK);
   };
-  auto load_of = [&](int j) -> int64_t { return (j < 0 || j >= p.nk) ? 0 : (int64_t)j * BK; };
+  // First HBM row copied by this wave for stage x of block j.
+  auto copy_row_of = [&](int j, int x) -> int64_t {
+    return ((j < 0 || j >= p.nk) ? 0 : (int64_t)j * BK) + (x % SPB) * 64 + wave * 16;
+  };
+  // Real keys among this wave's 32 keys of stage x of a block with nv real keys.
+  auto nvs_of = [&](int nv, int x) { return min(max(nv - (x % SPB) * 64 - kh * 32, 0), 32); };
 
   f32x16 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-  // Row sums of P come out of the matrix core: ones(32 x 16) x P^T puts the
-  // sum over a 16-key step into every row of the accumulator (one query per
-  // lane); entry 0 is the one kept.
-  f32x16 lacc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   const float sl2 = p.scale_log2;
 
-  // LDS element offsets that do not depend on the block.
-  const int sw = swz<CPR>(col);  // swizzle of K rows 32 kt + col
+  // LDS element offsets (within a stage) that do not depend on the stage.
+  const int sw = swz<CPR>(col);  // swizzle of K row 32 kh + col
   int koffs[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koffs[ks] = col * D + (((2 * ks + half) ^ sw) << 3);
+  for (int ks = 0; ks < KS; ++ks) koffs[ks] = (32 * kh + col) * D + (((2 * ks + half) ^ sw) << 3);
   const int g16 = lane >> 4, j16 = lane & 15, tq = j16 >> 2, q4 = j16 & 3;
   int voffs[DT][2];
 #pragma unroll
@@ -276,82 +283,89 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int d = dt * 32 + 16 * (g16 & 1) + 4 * q4;
-      const int row = 8 * c2 + 4 * half + tq;  // + multiples of 16
-      voffs[dt][c2] = row * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
+      const int row = 8 * c2 + 4 * half + tq;  // + 32 kh + 16 per key step
+      voffs[dt][c2] = (32 * kh + row) * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
     }
 
-  // Softmax state of the sub-tile about to be finished.
-  float m_run = -__builtin_inff();  // reference max (log2 units) of this row
-  float m_use = 0.0f, alpha = 1.0f;
+  // Softmax state of this lane's query row over this wave's keys.
+  float m_run = -__builtin_inff();  // reference max (log2 units)
+  float m_use = 0.0f;               // m_run, or 0 while it is -inf
+  float alpha = 1.0f;
+  float lsum = 0.0f;                // this lane's part of the row sum, relative to m_use
   bool need = false;
-  // Mask, row max and reference update for a freshly computed S (keys of the
-  // sub-tile at or past `nvs` are padding).
-  auto mask = [&](f32x16 (&sd)[KT], int nvs) {
-    if (nvs < SUB) {  // only sub-tiles that hold padding (uniform branch)
+  // Keys of the wave's 32 at or past `nvs` are padding.
+  auto mask = [&](f32x16& sd, int nvs) {
+    if (nvs < 32) {  // only stages that hold padding (uniform branch)
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          sd[kt][r] = key < nvs ? sd[kt][r] : -__builtin_inff();
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = (r >> 2) * 8 + half * 4 + (r & 3);
+        sd[r] = key < nvs ? sd[r] : -__builtin_inff();
+      }
     }
   };
-  auto prep = [&](f32x16 (&sd)[KT]) {
+  // Reference update from the lane's partial row maximum of a fresh S.
+  auto prep_tail = [&](float mxl) {
+    // When no lane's partial maximum clears its row's reference by the slack,
+    // neither does any row maximum and nothing changes (the usual case after
+    // the first stages): the cross-lane step is skipped.
     float mx = -__builtin_inff();
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        mx = __builtin_fmaxf(mx, __builtin_fmaxf(sd[kt][r], sd[kt][r + 1]));
-    mx = max_with_other_half(mx) * sl2;
-    need = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(mxl * sl2 > m_run + kRescaleSlack) != 0)
+      mx = max_with_other_half(mxl) * sl2;
+    const bool moves = mx > m_run + kRescaleSlack;
+    // While the reference is -inf no key has contributed: nothing to rescale.
+    need = moves && m_run != -__builtin_inff();
     const float e_alpha = __builtin_amdgcn_exp2f(m_run - mx);
     alpha = need ? e_alpha : 1.0f;
-    m_run = need ? mx : m_run;
+    m_run = moves ? mx : m_run;
     m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
   };
+  auto prep = [&](const f32x16& sd) {
+    float mxl = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(sd[r], sd[r + 1]));
+    prep_tail(mxl);
+  };
 
-  // Block bookkeeping: nv0 = real keys of block n; (j1, nv1) block n+1;
-  // (j2, nv2) block n+2.
-  int nv0 = 0, j1 = -1, nv1 = 0, j2 = -1, nv2 = 0;
-  f32x16 sA[KT], sB[KT];
+  // Blocks around the current stage u (in block n = u / SPB):
+  // (j0, nv0) block n, (j1, nv1) block n + 1, (j2, nv2) block n + 2.
+  int j0 = -1, nv0 = 0, j1 = -1, nv1 = 0, j2 = -1, nv2 = 0;
+  f32x16 sA, sB;
 
-  if (nblk > 0) {
-    const int j0 = block_of(0);
+  if (nst > 0) {
+    j0 = block_of(0);
     nv0 = nvalid_of(j0);
-    kcopy.issue(kbase + load_of(j0) * p.ks1, 0);
-    vcopy.issue(vbase + load_of(j0) * p.vs1, 0);
     if (nblk > 1) {
       j1 = block_of(1);
       nv1 = nvalid_of(j1);
-      kcopy.issue(kbase + load_of(j1) * p.ks1, TILE * 2);
+    }
+    kcopy.issue(kbase + copy_row_of(j0, 0) * p.ks1, k_stage(0));
+    vcopy.issue(vbase + copy_row_of(j0, 0) * p.vs1, v_stage(0));
+    if (nst > 1) {
+      const int jn = (SPB == 1) ? j1 : j0;
+      kcopy.issue(kbase + copy_row_of(jn, 1) * p.ks1, k_stage(1));
     }
     wait_vmcnt<0>();
     lds_barrier();
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int r = 0; r < 16; ++r) sA[r] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sA[kt][r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + kt * 32 * D + koffs[ks]);
-        sA[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sA[kt], 0, 0, 0);
-      }
-    mask(sA, nv0);
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + koffs[ks]);
+      sA = mfma(a, qf[ks], sA);
+    }
+    mask(sA, nvs_of(nv0, 0));
     prep(sA);
   }
 
-  // One pipeline step on sub-tile `sub` of block n. KP / VP are the LDS
-  // buffers read in this step (K of the next sub-tile, V of this one).
-  auto step = [&](auto kp_c, auto vp_c, int n, int sub, f32x16 (&s_cur)[KT],
-                  f32x16 (&s_nxt)[KT]) {
+  // One pipeline step on stage u. KP: the K stage read in this step (that of
+  // stage u + 1); VP: the V stage (that of stage u). Copies issued here: V of
+  // u + 1 into V stage VP ^ 1 and K of u + 2 into K stage KP ^ 1; both were
+  // last read in the previous step, which every wave has left at the barrier.
+  auto step = [&](auto kp_c, auto vp_c, int u, f32x16& s_cur, f32x16& s_nxt) {
     constexpr int KP = decltype(kp_c)::value;
     constexpr int VP = decltype(vp_c)::value;
-    const bool last_sub = sub == SPB - 1;
-    const bool has_next = !last_sub || n + 1 < nblk;
+    const bool last_sub = (u % SPB) == SPB - 1;
+    const int n = u / SPB;
     if (last_sub) {
       j2 = (n + 2 < nblk) ? block_of(n + 2) : -1;
       nv2 = (n + 2 < nblk) ? nvalid_of(j2) : 0;
@@ -359,86 +373,102 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     // ---- the step's single synchronisation point.
     wait_vmcnt<0>();
     lds_barrier();
-    if (sub == 0 && n + 1 < nblk) vcopy.issue(vbase + load_of(j1) * p.vs1, (VP ^ 1) * TILE * 2);
-    if (last_sub && n + 2 < nblk) kcopy.issue(kbase + load_of(j2) * p.ks1, (KP ^ 1) * TILE * 2);
-    const uint16_t* kb = Ks + KP * TILE + (last_sub ? 0 : (sub + 1) * SUB * D);
-    const uint16_t* vb = Vs + VP * TILE + sub * SUB * D;
-    if (sub == 0 && nv0 < BK) {
-      // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows.
-      constexpr int NT = NW * 64;
-      uint4* vz = reinterpret_cast<uint4*>(Vs + VP * TILE + nv0 * D);
-      const int nz = (BK - nv0) * D / 8;
-      for (int e = threadIdx.x; e < nz; e += NT) vz[e] = make_uint4(0, 0, 0, 0);
-      lds_barrier();
+    const bool v_next = u + 1 < nst, k_next = u + 2 < nst;
+    const uint16_t* v_rows =
+        vbase + copy_row_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) * p.vs1;
+    const uint16_t* k_rows = kbase + copy_row_of((SPB == 1) ? j2 : j1, u + 2) * p.ks1;
+    const uint16_t* kb = smem + KP * STAGE;
+    uint16_t* vb = smem + (2 + VP) * STAGE;
+    const int nvs = nvs_of(nv0, u);
+    if (nvs < 32) {
+      // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows
+      // (both waves of this key half write the same zeros).
+      uint4* vz = reinterpret_cast<uint4*>(vb + (32 * kh + nvs) * D);
+      const int nz = (32 - nvs) * D / 8;
+      for (int e = lane; e < nz; e += 64) vz[e] = make_uint4(0, 0, 0, 0);
     }
-    // Lazy rescale of the running output (rare after the first sub-tiles).
+    // Lazy rescale of the running output (rare after the first stages).
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      lacc[0] *= alpha;
+      lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
 
-    // ---- (a) S[u+1] = K Q^T || exponentials of P[u] || V^T reads.
+    // ---- (a) S[u+1] = K Q^T || exponentials of P[u] || V^T reads || copies.
+    bf16x8 pf[2];
+    bf16x4 vf[2][DT][2];
+    constexpr int EXP_PER = 16 / KS;  // exponentials per MFMA slot
+    constexpr int NVRD = 2 * DT * 2;  // V^T reads of the step
+    constexpr int VRD_PER = NVRD / KS;
+    static_assert(NVRD % KS == 0, "V reads per slot");
+    bf16x8 kf[3];
+    kf[0] = *reinterpret_cast<const bf16x8*>(kb + koffs[0]);
+    kf[1] = *reinterpret_cast<const bf16x8*>(kb + koffs[1]);
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[kt][r] = 0.0f;
-    bf16x8 pf[2 * KT];
-    bf16x4 vf[2 * KT][DT][2];
-    constexpr int EXP_PER = (2 * KT * 8) / NQK;   // exponentials per MFMA slot
-    constexpr int VRD_PER = (2 * KT * DT * 2) / NQK;  // V reads per MFMA slot
-    // K fragments are read two MFMA slots ahead of their use.
-    constexpr int KPF = 2;
-    bf16x8 kf[KPF + 1];
-#pragma unroll
-    for (int k = 0; k < KPF; ++k)
-      kf[k] = *reinterpret_cast<const bf16x8*>(kb + (k % KT) * 32 * D + koffs[k / KT]);
-#pragma unroll
-    for (int k = 0; k < NQK; ++k) {
-      const int ks = k / KT, kt = k % KT;
-      if (k + KPF < NQK)
-        kf[(k + KPF) % (KPF + 1)] = *reinterpret_cast<const bf16x8*>(
-            kb + ((k + KPF) % KT) * 32 * D + koffs[(k + KPF) / KT]);
-      s_nxt[kt] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k % (KPF + 1)], qf[ks], s_nxt[kt], 0, 0, 0);
+    for (int k = 0; k < KS; ++k) {
+      if (k + 2 < KS) kf[(k + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + koffs[k + 2]);
+      s_nxt = mfma(kf[k % 3], qf[k], s_nxt);
+      // One copy instruction per slot (V of u + 1, then K of u + 2).
+      if constexpr (KS == 2 * Copy::NL) {
+        if (k < Copy::NL) {
+          if (v_next) vcopy.issue_one(k, v_rows, v_stage(VP ^ 1));
+        } else {
+          if (k_next) kcopy.issue_one(k - Copy::NL, k_rows, k_stage(KP ^ 1));
+        }
+      } else {
+        if (k == 0) {
+          if (v_next) vcopy.issue(v_rows, v_stage(VP ^ 1));
+          if (k_next) kcopy.issue(k_rows, k_stage(KP ^ 1));
+        }
+      }
 #pragma unroll
       for (int x = 0; x < EXP_PER; ++x) {
-        const int idx = k * EXP_PER + x;           // element of P[u], 0 .. 16 KT - 1
-        const int pk = idx / 8, pe = idx % 8;      // fragment and slot
-        const int skt = pk / 2, sr = 8 * (pk % 2) + pe;
-        pf[pk][pe] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[skt][sr], sl2, -m_use));
+        const int r = k * EXP_PER + x;
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], sl2, -m_use));
+        // Pin the exponential to this slot: without it the compiler sinks
+        // the softmax below the masking branch, after every QK^T MFMA.
+        asm volatile("" : "+v"(e));
+        lsum += e;
+        pf[r / 8][r % 8] = (__bf16)e;
       }
 #pragma unroll
       for (int x = 0; x < VRD_PER; ++x) {
-        const int idx = k * VRD_PER + x;           // 0 .. 4 KT DT - 1
+        const int idx = k * VRD_PER + x;
         const int ks2 = idx / (DT * 2), dt = (idx / 2) % DT, c2 = idx % 2;
-        const int kt2 = ks2 / 2, s2 = ks2 % 2;
         vf[ks2][dt][c2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(vb + (kt2 * 32 + 16 * s2) * D + voffs[dt][c2]));
+            (lds_bf16x4*)(vb + 16 * ks2 * D + voffs[dt][c2]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // With no next sub-tile, S[u+1] is a dummy product and every key of it
+    // With no next stage, S[u+1] is a dummy product and every key of it
     // counts as padding, which leaves the softmax state unchanged.
-    const int nvs_next = !has_next ? 0 : (last_sub ? nv1 : nv0 - (sub + 1) * SUB);
+    const int nvs_next = (u + 1 < nst) ? nvs_of((SPB == 1 || last_sub) ? nv1 : nv0, u + 1) : 0;
     mask(s_nxt, nvs_next);
-    // ---- (b) O += V^T P[u]^T and row sums || row max of S[u+1].
+    // ---- (b) O += V^T P[u]^T || row max of S[u+1].
+    float mxl = -__builtin_inff();
+    constexpr int NPV = 2 * DT;
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2 * KT; ++ks2) {
-      lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pf[ks2], lacc, 0, 0, 0);
+    for (int sl = 0; sl < NPV; ++sl) {
+      const int ks2 = sl / DT, dt = sl % DT;
+      const bf16x8 av =
+          __builtin_shufflevector(vf[ks2][dt][0], vf[ks2][dt][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = mfma(av, pf[ks2], o[dt]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const bf16x8 av =
-            __builtin_shufflevector(vf[ks2][dt][0], vf[ks2][dt][1], 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pf[ks2], o[dt], 0, 0, 0);
+      for (int it = sl * 8 / NPV; it < (sl + 1) * 8 / NPV; ++it) {
+        mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(s_nxt[2 * it], s_nxt[2 * it + 1]));
+        asm volatile("" : "+v"(mxl));
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    prep(s_nxt);
+    prep_tail(mxl);
 
     if (last_sub) {
+      j0 = j1;
       nv0 = nv1;
       j1 = j2;
       nv1 = nv2;
@@ -447,78 +477,107 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 
   using C0 = std::integral_constant<int, 0>;
   using C1 = std::integral_constant<int, 1>;
-  // Steps in order, two blocks per loop turn so that the LDS buffers and the
-  // S registers alternate statically.
-  for (int n = 0; n < nblk; n += 2) {
-    if constexpr (SPB == 1) {
-      step(C1{}, C0{}, n, 0, sA, sB);
-      if (n + 1 < nblk) step(C0{}, C1{}, n + 1, 0, sB, sA);
-    } else {
-      step(C0{}, C0{}, n, 0, sA, sB);
-      step(C1{}, C0{}, n, 1, sB, sA);
-      if (n + 1 < nblk) {
-        step(C1{}, C1{}, n + 1, 0, sA, sB);
-        step(C0{}, C1{}, n + 1, 1, sB, sA);
-      }
-    }
+  // Two stages per loop turn so that the LDS stages and the S registers
+  // alternate statically.
+  for (int u = 0; u < nst; u += 2) {
+    step(C1{}, C0{}, u, sA, sB);
+    if (u + 1 < nst) step(C0{}, C1{}, u + 1, sB, sA);
   }
 
-  // ---- epilogue: O^T lane layout is query col, d = dt*32 + (r/4)*8 + half*4 + r%4.
-  const float l_run = lacc[0];
+  // ---- epilogue: merge the two key halves of each query half. Wave
+  // (qh, kh) finishes output tiles [kh DT/2, (kh + 1) DT/2) and hands the
+  // other half of its tiles, its reference and its row sum to wave
+  // (qh, 1 - kh) through LDS (free once every wave has left the loop).
+  const float ltot = sum_with_other_half(lsum);
+  constexpr int HT = DT / 2;   // output tiles finished per wave
+  constexpr int XR = HT * 16;  // accumulator registers handed over
+  lds_barrier();
+  float* xo = reinterpret_cast<float*>(smem) + wave * (XR + 2) * 64;
+  const float* yo = reinterpret_cast<const float*>(smem) + (wave ^ 1) * (XR + 2) * 64;
+  auto hand_over = [&](auto first_c) {
+    constexpr int F = decltype(first_c)::value;
+#pragma unroll
+    for (int x = 0; x < HT; ++x)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xo[(x * 16 + r) * 64 + lane] = o[F + x][r];
+  };
+  if (kh == 0)
+    hand_over(std::integral_constant<int, HT>{});
+  else
+    hand_over(std::integral_constant<int, 0>{});
+  xo[XR * 64 + lane] = m_use;
+  xo[(XR + 1) * 64 + lane] = ltot;
+  lds_barrier();
+  const float m2 = yo[XR * 64 + lane], l2 = yo[(XR + 1) * 64 + lane];
+  const bool e1 = ltot > 0.0f, e2 = l2 > 0.0f;
+  const float mm = __builtin_fmaxf(e1 ? m_use : -__builtin_inff(), e2 ? m2 : -__builtin_inff());
+  const float a1 = e1 ? __builtin_amdgcn_exp2f(m_use - mm) : 0.0f;
+  const float a2 = e2 ? __builtin_amdgcn_exp2f(m2 - mm) : 0.0f;
+  const float l_run = ltot * a1 + l2 * a2;
   const bool row_ok = qrow < p.q_valid && l_run > 0.0f;
   const float inv = row_ok ? 1.0f / l_run : 0.0f;
+  const float c1 = a1 * inv, c2 = a2 * inv;
+  // O^T lane layout: query col, d = dt*32 + (r/4)*8 + half*4 + r%4.
   uint16_t* op = p.o + (int64_t)b * p.os0 + (int64_t)qrow * p.os1 + (int64_t)h * p.os2;
+  auto finish = [&](auto first_c) {
+    constexpr int F = decltype(first_c)::value;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int x = 0; x < HT; ++x)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      bf16x4 vv;
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4 vv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] = (__bf16)(row_ok ? o[dt][rg * 4 + e] * inv : 0.0f);
-      *reinterpret_cast<bf16x4*>(op + dt * 32 + rg * 8 + half * 4) = vv;
-    }
-  if (p.lse != nullptr && half == 0) {
-    const float lse = row_ok ? (m_run + __builtin_log2f(l_run)) * 0.69314718055994531f
+        for (int e = 0; e < 4; ++e) {
+          const int r = rg * 4 + e;
+          const float v = o[F + x][r] * c1 + yo[(x * 16 + r) * 64 + lane] * c2;
+          vv[e] = (__bf16)(row_ok ? v : 0.0f);
+        }
+        *reinterpret_cast<bf16x4*>(op + (F + x) * 32 + rg * 8 + half * 4) = vv;
+      }
+  };
+  if (kh == 0)
+    finish(std::integral_constant<int, 0>{});
+  else
+    finish(std::integral_constant<int, HT>{});
+  if (p.lse != nullptr && kh == 0 && half == 0) {
+    const float lse = row_ok ? (mm + __builtin_log2f(l_run)) * 0.69314718055994531f
                              : -__builtin_inff();
     p.lse[((int64_t)b * p.hq + h) * p.q_len + qrow] = lse;
   }
 }
 
-template <int D, int BQ, int BK, bool DENSE>
-__global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int BK, bool DENSE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * BK * D];
-  attn_fwd_body<D, BQ, BK, DENSE>(p, Ks, Vs);
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * 64 * D];
+  attn_fwd_body<D, BK, DENSE>(p, smem);
 }
 
-template <int D, int BQ, int BK, bool DENSE>
+template <int D, int BK, bool DENSE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BQ, BK, DENSE>), dim3(p.n_wg), dim3(BQ * 2), 0, stream,
-                     p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, DENSE>), dim3(p.n_wg), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int BQ, int BK>
+template <int D, int BK>
 hipError_t launch_mode(const AttnParams& p, bool dense, hipStream_t stream) {
-  return dense ? launch_one<D, BQ, BK, true>(p, stream) : launch_one<D, BQ, BK, false>(p, stream);
+  return dense ? launch_one<D, BK, true>(p, stream) : launch_one<D, BK, false>(p, stream);
 }
 
 template <int D>
-hipError_t launch_geom(const AttnParams& p, int bq, int bk, bool dense, hipStream_t stream) {
-  if (bq == 64 && bk == 64) return launch_mode<D, 64, 64>(p, dense, stream);
-  if (bq == 64 && bk == 128) return launch_mode<D, 64, 128>(p, dense, stream);
-  if (bq == 128 && bk == 64) return launch_mode<D, 128, 64>(p, dense, stream);
-  return launch_mode<D, 128, 128>(p, dense, stream);
+hipError_t launch_geom(const AttnParams& p, int bk, bool dense, hipStream_t stream) {
+  if (bk == 64) return launch_mode<D, 64>(p, dense, stream);
+  return launch_mode<D, 128>(p, dense, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, bool dense,
                             hipStream_t stream) {
+  (void)block_q;  // a query block of 128 rows is two 64-row workgroups (p.qparts)
   if (p.n_wg == 0) return hipSuccess;
-  if (head_dim == 128) return launch_geom<128>(p, block_q, block_k, dense, stream);
-  return launch_geom<64>(p, block_q, block_k, dense, stream);
+  if (head_dim == 128) return launch_geom<128>(p, block_k, dense, stream);
+  return launch_geom<64>(p, block_k, dense, stream);
 }
 
 }  // namespace bsattn
