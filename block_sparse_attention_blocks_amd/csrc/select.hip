@@ -190,13 +190,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 
 // ------------------------------------------------------ scores and top-k
 // Workgroup = R consecutive query blocks of one (batch, query head). Phase 1:
-// each thread scores one candidate KV block against the R pooled query rows
-// (the rows are wave-uniform and come through scalar loads). Phase 2: each
-// wave takes rows and selects the top blocks by bisection on the 32-bit
-// keys, then writes the list in ascending block order.
+// the block scores of a 16-row x 16-candidate tile come from the fp64 matrix
+// cores (v_mfma_f64_16x16x4_f64, 4 head-dim entries per step): A (16 x 4)
+// holds the pooled query rows, lane l carrying row l % 16, entry l / 16; B
+// (4 x 16) the pooled keys, lane l carrying candidate l % 16, entry l / 16;
+// entry e of the result in lane l is row 4 e + l / 16, candidate l % 16.
+// Every product of two fp32 values is exact in fp64 and each accumulation is
+// rounded once, so the rigorous error bound of an fp64 dot product applies.
+// Phase 2: each wave takes rows and selects the top blocks by bisection on
+// the 32-bit keys, then writes the list in ascending block order.
 template <int D, int R>
 __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
   extern __shared__ uint32_t keys_lds[];
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  constexpr int KST = D / 4;  // MFMA k-steps over D
   const int ncand = p.n_cand;
   const int ncp = (ncand + 63) & ~63;
   const int i0 = blockIdx.x * R;
@@ -211,37 +218,38 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
   const double* __restrict__ knorm = p.kn + ((int64_t)b * p.hkv + g) * p.nk;
   const double gamma2 = 2.0 * (double)(D + 2) * 0x1p-53;
 
-  for (int c0 = 0; c0 < ncand; c0 += 256) {
-    const int c = c0 + tid;
-    const bool act = c < ncand;
-    const int j = p.n_prefix_blocks + (act ? c : 0);
-    const float* kc = kcols + j;
-    double acc[R];
+  const int arow = lane & 15, kq = lane >> 4;
+  double qa[KST];
+  {
+    const double* qr = qrows + (int64_t)min(arow, nrows - 1) * D + kq;
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    for (int d = 0; d < D; d += 4) {
-      double kd[4];
+    for (int st = 0; st < KST; ++st) qa[st] = qr[4 * st];
+  }
+  const int ntiles = (ncand + 15) >> 4;
+  for (int tile = wave; tile < ntiles; tile += 4) {
+    const int c = tile * 16 + arow;  // candidate of this lane (B column, result column)
+    const int j = p.n_prefix_blocks + min(c, ncand - 1);
+    const float* kc = kcols + j + (int64_t)kq * p.nk;
+    float kb[KST];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kd[u] = (double)kc[(int64_t)(d + u) * p.nk];
+    for (int st = 0; st < KST; ++st) kb[st] = kc[(int64_t)(4 * st) * p.nk];
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const double* qr = qrows + (int64_t)min(r, nrows - 1) * D + d;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[r] = __builtin_fma(qr[u], kd[u], acc[r]);
-      }
-    }
-    if (act) {
+    for (int st = 0; st < KST; ++st)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[st], (double)kb[st], acc, 0, 0, 0);
+    if (c < ncand) {
       const double knj = knorm[j];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * e + kq;
         if (r < nrows) {
-          const double s = acc[r];
-          const double w = gamma2 * qnorm[r] * knj + __builtin_fabs(s) * 0x1p-52;
-          const float lo = (float)(s - w);
-          const float hi = (float)(s + w);
+          const double sc = acc[e];
+          const double w = gamma2 * qnorm[r] * knj + __builtin_fabs(sc) * 0x1p-52;
+          const float lo = (float)(sc - w);
+          const float hi = (float)(sc + w);
           float f = lo;
           if (__float_as_uint(lo) != __float_as_uint(hi))
-            f = exact_dot_rn32(qrows + (int64_t)r * D, kc, p.nk, D);
+            f = exact_dot_rn32(qrows + (int64_t)r * D, kcols + j, p.nk, D);
           keys_lds[r * ncp + c] = order_key(f);
         }
       }
@@ -265,21 +273,46 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
       int need_eq = 0;
       if (rsel > 0 && !take_all) {
         // Largest thr with #{key >= thr} >= rsel: the rsel-th largest key.
-        for (int bit = 31; bit >= 0; --bit) {
-          const uint32_t cand = thr | (1u << bit);
-          int count = 0;
+        // Every real key is at least order_key(-inf) > 0, so the 0 standing
+        // in for a missing candidate never counts.
+        if constexpr (R == 16) {
+          // At most 1024 candidates: the row's keys stay in registers.
+          uint32_t kreg[16];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            const int jj = m * 64 + lane;
+            kreg[m] = (m < M && jj < ncand) ? kr[jj] : 0u;
+          }
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int count = 0;
+#pragma unroll
+            for (int m = 0; m < 16; ++m)
+              if (m < M) count += __popcll(__ballot(kreg[m] >= cand));
+            if (count >= rsel) thr = cand;
+          }
+          int gt = 0;
+#pragma unroll
+          for (int m = 0; m < 16; ++m)
+            if (m < M) gt += __popcll(__ballot(kreg[m] > thr));
+          need_eq = rsel - gt;  // >= 1
+        } else {
+          for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = thr | (1u << bit);
+            int count = 0;
+            for (int m = 0; m < M; ++m) {
+              const int jj = m * 64 + lane;
+              count += __popcll(__ballot(jj < ncand && kr[jj] >= cand));
+            }
+            if (count >= rsel) thr = cand;
+          }
+          int gt = 0;
           for (int m = 0; m < M; ++m) {
             const int jj = m * 64 + lane;
-            count += __popcll(__ballot(jj < ncand && kr[jj] >= cand));
+            gt += __popcll(__ballot(jj < ncand && kr[jj] > thr));
           }
-          if (count >= rsel) thr = cand;
+          need_eq = rsel - gt;  // >= 1
         }
-        int gt = 0;
-        for (int m = 0; m < M; ++m) {
-          const int jj = m * 64 + lane;
-          gt += __popcll(__ballot(jj < ncand && kr[jj] > thr));
-        }
-        need_eq = rsel - gt;  // >= 1
       }
       for (int s = lane; s < p.n_forced; s += 64) out[s] = s;
       int pos = p.n_forced;
