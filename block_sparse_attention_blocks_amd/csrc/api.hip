@@ -95,7 +95,7 @@ attn_status validate_shape(const attn_shape* s, const char* fn) {
     return fail(ATTN_ERR_INVALID_ARG, fn, "softmax_scale is not finite");
   if (s->batch > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, fn, "batch %d > 65535", s->batch);
-  const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / 64);
+  const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / s->block_q);
   if (nwg > 0x7FFFFFFF) return fail(ATTN_ERR_UNSUPPORTED, fn, "grid too large");
   return ATTN_OK;
 }
@@ -221,8 +221,7 @@ attn_status run_attention(const char* fn, const attn_shape* s, const void* q, co
   p.n_forced = d.n_forced;
   p.n_cand = d.n_cand;
   p.idx_row_stride = dense ? 0 : idx_row_stride;
-  p.qparts = s->block_q / 64;
-  p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq * p.qparts);
+  p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq);
   p.scale_log2 = scale_of(s) * 1.4426950408889634f;
   if (p.n_wg == 0) return ok();
   st = check_device(fn);

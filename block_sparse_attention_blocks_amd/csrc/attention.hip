@@ -91,8 +91,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// HBM->LDS copy of this wave's 16 rows (rows 16 w .. 16 w + 15) of a 64-row
-// stage, with global_load_lds_dwordx4 in its scalar-base form: the LDS
+// HBM->LDS copy of this wave's RPW rows (rows RPW w .. RPW w + RPW - 1) of a
+// 64-row stage, with global_load_lds_dwordx4 in its scalar-base form: the LDS
 // destination comes from M0 and the HBM address is a 64-bit scalar base plus
 // a 32-bit per-lane offset, so a copy costs no vector ALU work. Instruction
 // `it` moves 64 x 16 bytes = RPI whole rows. The lane's chunk within its row
@@ -101,18 +101,20 @@ __device__ __forceinline__ void lds_barrier() {
 // The copies are issued from inline assembly, so the compiler does not track
 // them: every read of a stage is preceded by an explicit wait_vmcnt and a
 // workgroup barrier.
-template <int D>
+template <int D, int RPW>
 struct StageCopy {
   static constexpr int CPR = D / 8;
   static constexpr int RPI = 64 / CPR;
-  static constexpr int NL = 16 / RPI;  // instructions per wave and stage
+  static constexpr int NL = RPW / RPI;  // instructions per wave and stage
+  static_assert(NL * RPI == RPW && NL >= 1, "rows per wave");
   uint32_t voff[NL];                   // per-lane byte offsets
 
-  __device__ __forceinline__ void init(int64_t row_stride, int lane) {
+  // The swizzle follows the row's position in the stage (RPW wave + row).
+  __device__ __forceinline__ void init(int64_t row_stride, int lane, int wave) {
 #pragma unroll
     for (int it = 0; it < NL; ++it) {
       const int row = it * RPI + lane / CPR;
-      const int lch = (lane % CPR) ^ swz<CPR>(row);
+      const int lch = (lane % CPR) ^ swz<CPR>(wave * RPW + row);
       voff[it] = (uint32_t)((row * row_stride + lch * 8) * 2);
     }
   }
@@ -164,7 +166,7 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int BK, bool DENSE>
+template <int D, int BK, int NQG, bool DENSE>
 __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ smem) {
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;     // MFMA k-steps over D (QK^T MFMAs per stage)
@@ -172,7 +174,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   constexpr int SPB = BK / 64;   // 64-key stages per block
   constexpr int STAGE = 64 * D;  // elements of one K or V stage
   static_assert(SPB == 1 || SPB == 2, "block_k 64 or 128");
-  using Copy = StageCopy<D>;
+  constexpr int NW = 2 * NQG;    // waves: NQG query groups of 32 rows x 2 key halves
+  constexpr int RPW = 64 / NW;   // stage rows copied by each wave
+  using Copy = StageCopy<D, RPW>;
   // A row moves its reference max only when a stage max exceeds it by more
   // than this many powers of two; until then probabilities are taken against
   // the stale max and stay below 2^8, far from fp32 or bf16 overflow.
@@ -180,19 +184,18 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qh = wave >> 1;  // query half
+  const int qh = wave >> 1;  // 32-row query group
   const int kh = wave & 1;   // key half of every stage
   const int col = lane & 31;
   const int half = lane >> 5;
 
   // Workgroup w runs on XCD w % 8; give each XCD a contiguous range of the
-  // (batch, KV head, query block, head-in-group, 64-row part) order.
+  // (batch, KV head, query block, head-in-group) order.
   const int nwg = p.n_wg;
   const int w = blockIdx.x;
   const int xcd = w & 7, per = nwg >> 3, rem = nwg & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
-  const int part = lin % p.qparts;
-  int t = lin / p.qparts;
+  int t = lin;
   const int hig = t % p.group;
   t /= p.group;
   const int i = t % p.nq;
@@ -200,7 +203,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int g = t % p.hkv;
   const int b = t / p.hkv;
   const int h = g * p.group + hig;
-  const int row0 = i * (64 * p.qparts) + part * 64;
+  const int row0 = i * (32 * NQG);
   const int qrow = row0 + 32 * qh + col;
 
   // Q^T fragments (B operand): the lane holds q[qrow][16 ks + 8 half .. +7].
@@ -230,12 +233,12 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
   Copy kcopy, vcopy;
-  kcopy.init(p.ks1, lane);
-  vcopy.init(p.vs1, lane);
-  // LDS: K stages 0, 1 then V stages 0, 1; this wave copies rows 16 wave ..
+  kcopy.init(p.ks1, lane, wave);
+  vcopy.init(p.vs1, lane, wave);
+  // LDS: K stages 0, 1 then V stages 0, 1; this wave copies rows RPW wave ..
   const uint32_t smem_addr =
       (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)smem);
-  const uint32_t wcopy = (uint32_t)(wave * 16 * D * 2);
+  const uint32_t wcopy = (uint32_t)(wave * RPW * D * 2);
   auto k_stage = [&](int s) { return smem_addr + (uint32_t)(s * STAGE * 2) + wcopy; };
   auto v_stage = [&](int s) { return smem_addr + (uint32_t)((2 + s) * STAGE * 2) + wcopy; };
 
@@ -259,7 +262,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   };
   // First HBM row copied by this wave for stage x of block j.
   auto copy_row_of = [&](int j, int x) -> int64_t {
-    return ((j < 0 || j >= p.nk) ? 0 : (int64_t)j * BK) + (x % SPB) * 64 + wave * 16;
+    return ((j < 0 || j >= p.nk) ? 0 : (int64_t)j * BK) + (x % SPB) * 64 + wave * RPW;
   };
   // Real keys among this wave's 32 keys of stage x of a block with nv real keys.
   auto nvs_of = [&](int nv, int x) { return min(max(nv - (x % SPB) * 64 - kh * 32, 0), 32); };
@@ -412,17 +415,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     for (int k = 0; k < KS; ++k) {
       if (k + 2 < KS) kf[(k + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + koffs[k + 2]);
       s_nxt = mfma(kf[k % 3], qf[k], s_nxt);
-      // One copy instruction per slot (V of u + 1, then K of u + 2).
-      if constexpr (KS == 2 * Copy::NL) {
-        if (k < Copy::NL) {
-          if (v_next) vcopy.issue_one(k, v_rows, v_stage(VP ^ 1));
+      // The copy instructions spread evenly over the slots (V of u + 1, then
+      // K of u + 2).
+      static_assert(KS % (2 * Copy::NL) == 0, "copy slots");
+      constexpr int CEVERY = KS / (2 * Copy::NL);
+      if (k % CEVERY == 0) {
+        const int c = k / CEVERY;
+        if (c < Copy::NL) {
+          if (v_next) vcopy.issue_one(c, v_rows, v_stage(VP ^ 1));
         } else {
-          if (k_next) kcopy.issue_one(k - Copy::NL, k_rows, k_stage(KP ^ 1));
-        }
-      } else {
-        if (k == 0) {
-          if (v_next) vcopy.issue(v_rows, v_stage(VP ^ 1));
-          if (k_next) kcopy.issue(k_rows, k_stage(KP ^ 1));
+          if (k_next) kcopy.issue_one(c - Copy::NL, k_rows, k_stage(KP ^ 1));
         }
       }
 #pragma unroll
@@ -546,38 +548,52 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   }
 }
 
-template <int D, int BK, bool DENSE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_fwd_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * 64 * D];
-  attn_fwd_body<D, BK, DENSE>(p, smem);
+// LDS of a workgroup: the four stages, or the epilogue's hand-over area if
+// that is larger (eight waves at head dim 128).
+template <int D, int NQG>
+constexpr int smem_elems() {
+  constexpr int stages = 4 * 64 * D;
+  constexpr int handover = 2 * NQG * ((D / 64) * 16 + 2) * 64 * 2;  // floats -> bf16 units
+  return stages > handover ? stages : handover;
 }
 
-template <int D, int BK, bool DENSE>
+template <int D, int BK, int NQG, bool DENSE>
+__global__ void __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_fwd_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<D, NQG>()];
+  attn_fwd_body<D, BK, NQG, DENSE>(p, smem);
+}
+
+template <int D, int BK, int NQG, bool DENSE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, DENSE>), dim3(p.n_wg), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, DENSE>), dim3(p.n_wg), dim3(128 * NQG), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-template <int D, int BK>
+template <int D, int BK, int NQG>
 hipError_t launch_mode(const AttnParams& p, bool dense, hipStream_t stream) {
-  return dense ? launch_one<D, BK, true>(p, stream) : launch_one<D, BK, false>(p, stream);
+  return dense ? launch_one<D, BK, NQG, true>(p, stream)
+               : launch_one<D, BK, NQG, false>(p, stream);
 }
 
-template <int D>
+template <int D, int NQG>
 hipError_t launch_geom(const AttnParams& p, int bk, bool dense, hipStream_t stream) {
-  if (bk == 64) return launch_mode<D, 64>(p, dense, stream);
-  return launch_mode<D, 128>(p, dense, stream);
+  if (bk == 64) return launch_mode<D, 64, NQG>(p, dense, stream);
+  return launch_mode<D, 128, NQG>(p, dense, stream);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, bool dense,
                             hipStream_t stream) {
-  (void)block_q;  // a query block of 128 rows is two 64-row workgroups (p.qparts)
   if (p.n_wg == 0) return hipSuccess;
-  if (head_dim == 128) return launch_geom<128>(p, block_k, dense, stream);
-  return launch_geom<64>(p, block_k, dense, stream);
+  // One workgroup per query block: 4 waves for 64 rows, 8 waves for 128 rows.
+  if (head_dim == 128)
+    return block_q == 64 ? launch_geom<128, 2>(p, block_k, dense, stream)
+                         : launch_geom<128, 4>(p, block_k, dense, stream);
+  return block_q == 64 ? launch_geom<64, 2>(p, block_k, dense, stream)
+                       : launch_geom<64, 4>(p, block_k, dense, stream);
 }
 
 }  // namespace bsattn

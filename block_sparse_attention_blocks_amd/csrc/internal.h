@@ -25,8 +25,7 @@ struct AttnParams {
   int32_t n_forced;         // protected blocks holding a real key: [0, n_forced)
   int32_t n_cand;           // generation blocks holding a real key: [P, P + n_cand)
   int32_t idx_row_stride;
-  int32_t qparts;           // 64-row parts per query block (block_q / 64)
-  int32_t n_wg;             // workgroups in the grid: batch * hq * nq * qparts
+  int32_t n_wg;             // workgroups in the grid: batch * hq * nq
   float scale_log2;         // softmax scale * log2(e)
 };
 
