@@ -13,7 +13,9 @@ What it computes, step by step, in the order of the method:
                       prefix always kept, top-k with ties to the lower index;
 * ``attend``        - non-causal softmax attention over the selected blocks,
                       padded keys excluded, GQA head h -> KV head h // G;
-* ``dense``         - the same with every block selected.
+* ``dense``         - the same with every block selected;
+* ``dense_causal``  - causal dense attention, bottom-right aligned over the
+                      real tokens (the understanding pathway's self-attention).
 
 Sources (web pages): vllm-omni PR #8335 "[Core] Add shared block-sparse
 attention adapters with FlashAttention-4" (Purpose: selector producing
@@ -23,7 +25,9 @@ native MHA/MQA/GQA mapping; 75 % target sparsity); diffusers
 pairs with KV group i // repeats; ``build_gen_key_mask``: padded und and gen
 keys masked; ``cosmos3_cp_attention``: the generation pathway attends with full
 attention to cat(und, gen)); mstar PR #927 (automated review: default softmax
-scale head_dim**-0.5).
+scale head_dim**-0.5; bottom-right causal alignment of the dense pass);
+``cosmos3_cp_attention`` again for the understanding pathway's causal
+self-attention.
 
 Parity: every function here is pinned by CPU tests against closed forms,
 brute force, exact rational arithmetic and torch's fp64 SDPA; none is
@@ -31,10 +35,10 @@ brute force, exact rational arithmetic and torch's fp64 SDPA; none is
 """
 from .selector import keep_blocks, valid_key_mask, valid_query_mask, pool, block_scores, \
     select, select_from_scores, rn32_exact, widen_bf16
-from .attention import attend, attend_rows, dense, identity_selection
+from .attention import attend, attend_rows, dense, dense_causal, identity_selection, key_ranks
 
 __all__ = [
     "keep_blocks", "valid_key_mask", "valid_query_mask", "pool", "block_scores", "select",
     "select_from_scores", "rn32_exact", "widen_bf16", "attend", "attend_rows", "dense",
-    "identity_selection",
+    "dense_causal", "identity_selection", "key_ranks",
 ]

@@ -17,7 +17,12 @@ Semantics, each from the pages:
   per-query-head block indices/counts are what the backend executes);
 * softmax scale defaults to head_dim ** -0.5 (mstar PR #927, automated
   review);
-* padded query rows produce 0 and lse = -inf, as does a row with no valid key.
+* padded query rows produce 0 and lse = -inf, as does a row with no valid key;
+* causal dense attention (``dense_causal``): the understanding pathway
+  attends causally to itself (diffusers ``cosmos_parallel.py``,
+  ``cosmos3_cp_attention``, understanding pathway), with the causal diagonal
+  aligned to the bottom right (mstar PR #927, automated review: the dense
+  ragged wrapper keeps the FA3 call's bottom-right causal alignment).
 """
 from __future__ import annotations
 
@@ -151,3 +156,52 @@ def dense(layout: dict, q_bits, k_bits, v_bits):
     """Dense (0 % sparsity) attention: every KV block selected."""
     idx, cnt = identity_selection(layout)
     return attend(layout, q_bits, k_bits, v_bits, idx, cnt)
+
+
+def key_ranks(layout: dict) -> np.ndarray:
+    """Position of every key among the real keys, in key order (the prefix
+    segment's real keys, then the generation segment's); -1 for padding."""
+    kmask = valid_key_mask(layout)
+    return np.where(kmask, np.cumsum(kmask) - 1, -1)
+
+
+def dense_causal(layout: dict, q_bits, k_bits, v_bits):
+    """Causal dense attention, bottom-right aligned over the real tokens.
+
+    With n_k real keys and n_q = q_valid real query rows, real row t attends
+    the real keys of rank r <= t + (n_k - n_q): the last real row sees every
+    real key and each earlier row one key fewer. When n_k == n_q (a stream
+    attending to itself) this is the usual causal mask r <= t. Padding is
+    invisible: padded keys take no weight, padded rows give 0 and lse = -inf,
+    as does a real row left with no key (n_q > n_k). Returns o [B, q_len, Hq,
+    D] and lse [B, Hq, q_len] like ``attend``.
+    """
+    hq, hkv = layout["num_q_heads"], layout["num_kv_heads"]
+    grp = hq // hkv
+    scale = _scale(layout)
+    qmask = valid_query_mask(layout)
+    rank = key_ranks(layout)
+    n_k = int((rank >= 0).sum())
+    off = n_k - layout["q_valid"]
+    b_, lq, _, d = q_bits.shape
+    o = np.zeros((b_, lq, hq, d))
+    lse = np.full((b_, hq, lq), -np.inf)
+    t = np.nonzero(qmask)[0]
+    allowed = (rank[None, :] >= 0) & (rank[None, :] <= t[:, None] + off)   # [rows, keys]
+    live = allowed.any(axis=1)
+    if not live.any():
+        return o, lse
+    t, allowed = t[live], allowed[live]
+    for b in range(b_):
+        for g in range(hkv):
+            kg = widen_bf16(k_bits[b, :, g, :])
+            vg = np.where((rank >= 0)[:, None], widen_bf16(v_bits[b, :, g, :]), 0.0)
+            for h in range(g * grp, (g + 1) * grp):
+                qh = widen_bf16(q_bits[b, t, h, :])
+                logits = np.where(allowed, scale * (qh @ kg.T), -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                p = np.where(allowed, np.exp(logits - m), 0.0)
+                l = p.sum(axis=1, keepdims=True)
+                o[b, t, h] = (p @ vg) / l
+                lse[b, h, t] = (m + np.log(l))[:, 0]
+    return o, lse
