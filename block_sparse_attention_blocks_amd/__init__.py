@@ -47,8 +47,8 @@ class AttnShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_keep_blocks", "attn_select_workspace_size", "attn_select_blocks",
-           "attn_block_sparse_fwd", "attn_dense_fwd", "attn_query_support",
-           "attn_last_error", "attn_version")
+           "attn_block_sparse_fwd", "attn_dense_fwd", "attn_dense_causal_fwd",
+           "attn_query_support", "attn_last_error", "attn_version")
 
 
 def _load():
@@ -69,6 +69,8 @@ def _load():
     lib.attn_block_sparse_fwd.restype = I32
     lib.attn_dense_fwd.argtypes = [SH, P, P, P, P, P, P]
     lib.attn_dense_fwd.restype = I32
+    lib.attn_dense_causal_fwd.argtypes = [SH, P, P, P, P, P, P]
+    lib.attn_dense_causal_fwd.restype = I32
     lib.attn_query_support.argtypes = [SH]
     lib.attn_query_support.restype = I32
     lib.attn_last_error.argtypes = []
@@ -218,8 +220,10 @@ def block_sparse_attention(q, k, v, block_idx, block_cnt, layout, *, out=None, r
     return (out, lse) if return_lse else out
 
 
-def dense_attention(q, k, v, layout, *, out=None, return_lse=False, stream=None):
-    """Dense attention through the same kernel (attn_dense_fwd)."""
+def dense_attention(q, k, v, layout, *, causal=False, out=None, return_lse=False, stream=None):
+    """Dense attention through the same kernel (attn_dense_fwd), or, with
+    ``causal``, causal dense attention bottom-right aligned over the real
+    tokens (attn_dense_causal_fwd)."""
     import torch
     _check_tensor(q, "q", torch.bfloat16)
     for t, n in ((k, "k"), (v, "v")):
@@ -231,8 +235,9 @@ def dense_attention(q, k, v, layout, *, out=None, return_lse=False, stream=None)
         lse = torch.empty((int(layout["batch"]), int(layout["num_q_heads"]), int(layout["q_len"])),
                           dtype=torch.float32, device=q.device)
     shape = make_shape(layout, q=q, k=k, v=v, out=out)
-    _check(lib.attn_dense_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                              _ptr(lse), _stream_handle(stream)))
+    fn = lib.attn_dense_causal_fwd if causal else lib.attn_dense_fwd
+    _check(fn(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+              _stream_handle(stream)))
     return (out, lse) if return_lse else out
 
 

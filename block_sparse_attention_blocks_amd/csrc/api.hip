@@ -179,8 +179,9 @@ float scale_of(const attn_shape* s) {
 
 attn_status run_attention(const char* fn, const attn_shape* s, const void* q, const void* k,
                           const void* v, const int32_t* idx, const int32_t* cnt,
-                          int32_t idx_row_stride, void* out, float* lse, bool dense,
+                          int32_t idx_row_stride, void* out, float* lse, int mode,
                           hipStream_t stream) {
+  const bool dense = mode != bsattn::kSparse;
   attn_status st = validate_shape(s, fn);
   if (st != ATTN_OK) return st;
   st = validate_tensors(fn, q, k, v, out, lse);
@@ -221,12 +222,13 @@ attn_status run_attention(const char* fn, const attn_shape* s, const void* q, co
   p.n_forced = d.n_forced;
   p.n_cand = d.n_cand;
   p.idx_row_stride = dense ? 0 : idx_row_stride;
+  p.causal_off = (s->kv_prefix_valid + s->kv_suffix_valid) - s->q_valid;
   p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq);
   p.scale_log2 = scale_of(s) * 1.4426950408889634f;
   if (p.n_wg == 0) return ok();
   st = check_device(fn);
   if (st != ATTN_OK) return st;
-  const hipError_t e = bsattn::launch_attention(p, s->head_dim, s->block_q, s->block_k, dense, stream);
+  const hipError_t e = bsattn::launch_attention(p, s->head_dim, s->block_q, s->block_k, mode, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -334,12 +336,19 @@ attn_status attn_block_sparse_fwd(const attn_shape* s, const void* q, const void
                                   int32_t idx_row_stride, void* out, float* lse,
                                   hipStream_t stream) {
   return run_attention("attn_block_sparse_fwd", s, q, k, v, block_idx, block_cnt, idx_row_stride,
-                       out, lse, false, stream);
+                       out, lse, bsattn::kSparse, stream);
 }
 
 attn_status attn_dense_fwd(const attn_shape* s, const void* q, const void* k, const void* v,
                            void* out, float* lse, hipStream_t stream) {
-  return run_attention("attn_dense_fwd", s, q, k, v, nullptr, nullptr, 0, out, lse, true, stream);
+  return run_attention("attn_dense_fwd", s, q, k, v, nullptr, nullptr, 0, out, lse, bsattn::kDense,
+                       stream);
+}
+
+attn_status attn_dense_causal_fwd(const attn_shape* s, const void* q, const void* k, const void* v,
+                                  void* out, float* lse, hipStream_t stream) {
+  return run_attention("attn_dense_causal_fwd", s, q, k, v, nullptr, nullptr, 0, out, lse,
+                       bsattn::kCausal, stream);
 }
 
 attn_status attn_query_support(const attn_shape* s) {

@@ -7,17 +7,21 @@
 // softmax attention over the keys of the KV blocks listed for that
 // (batch, query head, query block), padded keys excluded, query head h
 // reading KV head h / G in place. The dense case is the same kernel with the
-// list "every non-empty block" generated in-kernel.
+// list "every non-empty block" generated in-kernel; the causal dense case
+// (the understanding pathway's causal self-attention in cosmos3_cp_attention,
+// bottom-right aligned as in mstar PR #927, automated review) cuts that list
+// at the block's last reachable key and masks the diagonal stages.
 //
-// Structure: one workgroup of four waves per 64 query rows (a 128-row query
-// block is two workgroups reading the same list). The keys are streamed in
-// stages of 64; wave (qh, kh) computes query rows [32 qh, 32 qh + 32) against
-// keys [32 kh, 32 kh + 32) of every stage, so both waves of a key half read
-// the same K and V rows from LDS. Each wave keeps its own partial softmax
-// state; the two key halves are merged once at the end. A wave needs fewer
-// than 256 registers, so two workgroups share a CU and every SIMD runs two
-// waves: while one wave waits (LDS, barrier, the HBM copies) the other
-// issues, and one wave's softmax overlaps the other's matrix products.
+// Structure: one workgroup per query block. Its rows form NQG = block_q / 32
+// query groups and the keys are streamed in stages of 64, split into two key
+// halves; wave (qh, kh) computes query rows [32 qh, 32 qh + 32) against keys
+// [32 kh, 32 kh + 32) of every stage, so every K/V stage in LDS feeds all the
+// block's rows. Each wave keeps its own partial softmax state; the two key
+// halves are merged once at the end. A wave needs fewer than 256 registers,
+// so every SIMD runs two waves (two 4-wave workgroups per CU at 64-row
+// blocks, one 8-wave workgroup at 128-row blocks): while one wave waits (LDS,
+// barrier, the HBM copies) the other issues, and one wave's softmax overlaps
+// the other's matrix products.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K fragment (A operand)
 //    comes from LDS, Q^T (B operand) stays in registers for the whole
 //    kernel. Each lane owns one query row and half of the 32 keys, so the
@@ -166,8 +170,10 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int BK, int NQG, bool DENSE>
+template <int D, int BK, int NQG, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ smem) {
+  constexpr bool DENSE = MODE != kSparse;    // the list is every non-empty block
+  constexpr bool CAUSAL = MODE == kCausal;   // ... cut to the causal range
   constexpr int CPR = D / 8;
   constexpr int KS = D / 16;     // MFMA k-steps over D (QK^T MFMAs per stage)
   constexpr int DT = D / 32;     // output 32-row tiles over D
@@ -220,7 +226,20 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 
   int nblk;
   const int32_t* idx_row = nullptr;
-  if constexpr (DENSE) {
+  if constexpr (CAUSAL) {
+    // Blocks whose first real key has a rank within reach of the block's last
+    // real row (rank <= t + causal_off); their real keys are ranked in block
+    // order: prefix block n from n BK, generation block m from
+    // kv_prefix_valid + m BK.
+    const int last_rank = min(row0 + 32 * NQG, p.q_valid) - 1 + p.causal_off;
+    int n_pre = 0, n_gen = 0;
+    if (last_rank >= 0) {
+      n_pre = min(p.n_forced, last_rank / BK + 1);
+      if (last_rank >= p.kv_prefix_valid)
+        n_gen = min(p.n_cand, (last_rank - p.kv_prefix_valid) / BK + 1);
+    }
+    nblk = n_pre + n_gen;
+  } else if constexpr (DENSE) {
     nblk = p.n_forced + p.n_cand;
   } else {
     const int64_t row_id = ((int64_t)b * p.hq + h) * p.nq + i;
@@ -266,6 +285,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   };
   // Real keys among this wave's 32 keys of stage x of a block with nv real keys.
   auto nvs_of = [&](int nv, int x) { return min(max(nv - (x % SPB) * 64 - kh * 32, 0), 32); };
+  // Rank among the real keys of the first of this wave's 32 keys of stage x
+  // of block j (causal mode; blocks are segment aligned and real keys lead
+  // each segment).
+  auto rank0_of = [&](int j, int x) {
+    const int k0 = j * BK + (x % SPB) * 64 + 32 * kh;
+    return j < p.n_prefix_blocks ? k0 : p.kv_prefix_valid + (k0 - p.kv_prefix_len);
+  };
 
   f32x16 o[DT];
 #pragma unroll
@@ -296,13 +322,20 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   float alpha = 1.0f;
   float lsum = 0.0f;                // this lane's part of the row sum, relative to m_use
   bool need = false;
-  // Keys of the wave's 32 at or past `nvs` are padding.
-  auto mask = [&](f32x16& sd, int nvs) {
-    if (nvs < 32) {  // only stages that hold padding (uniform branch)
+  // Keys of the wave's 32 at or past `nvs` are padding. In causal mode key
+  // kk also has rank rank0 + kk, and row qrow keeps ranks <= qrow + causal_off.
+  auto mask = [&](f32x16& sd, int nvs, int rank0) {
+    int lim = nvs;      // this lane keeps keys [0, lim)
+    bool any = nvs < 32;
+    if constexpr (CAUSAL) {
+      lim = min(nvs, qrow + p.causal_off - rank0 + 1);
+      any = any || (row0 + 32 * qh + p.causal_off - rank0 + 1 < 32);  // the wave's first row
+    }
+    if (any) {  // only stages that hold padding or cross the diagonal (uniform branch)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = (r >> 2) * 8 + half * 4 + (r & 3);
-        sd[r] = key < nvs ? sd[r] : -__builtin_inff();
+        sd[r] = key < lim ? sd[r] : -__builtin_inff();
       }
     }
   };
@@ -356,7 +389,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + koffs[ks]);
       sA = mfma(a, qf[ks], sA);
     }
-    mask(sA, nvs_of(nv0, 0));
+    mask(sA, nvs_of(nv0, 0), CAUSAL ? rank0_of(j0, 0) : 0);
     prep(sA);
   }
 
@@ -450,7 +483,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     // With no next stage, S[u+1] is a dummy product and every key of it
     // counts as padding, which leaves the softmax state unchanged.
     const int nvs_next = (u + 1 < nst) ? nvs_of((SPB == 1 || last_sub) ? nv1 : nv0, u + 1) : 0;
-    mask(s_nxt, nvs_next);
+    mask(s_nxt, nvs_next,
+         CAUSAL ? rank0_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) : 0);
     // ---- (b) O += V^T P[u]^T || row max of S[u+1].
     float mxl = -__builtin_inff();
     constexpr int NPV = 2 * DT;
@@ -557,43 +591,47 @@ constexpr int smem_elems() {
   return stages > handover ? stages : handover;
 }
 
-template <int D, int BK, int NQG, bool DENSE>
+template <int D, int BK, int NQG, int MODE>
 __global__ void __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<D, NQG>()];
-  attn_fwd_body<D, BK, NQG, DENSE>(p, smem);
+  attn_fwd_body<D, BK, NQG, MODE>(p, smem);
 }
 
-template <int D, int BK, int NQG, bool DENSE>
+template <int D, int BK, int NQG, int MODE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, DENSE>), dim3(p.n_wg), dim3(128 * NQG), 0,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, MODE>), dim3(p.n_wg), dim3(128 * NQG), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 template <int D, int BK, int NQG>
-hipError_t launch_mode(const AttnParams& p, bool dense, hipStream_t stream) {
-  return dense ? launch_one<D, BK, NQG, true>(p, stream)
-               : launch_one<D, BK, NQG, false>(p, stream);
+hipError_t launch_mode(const AttnParams& p, int mode, hipStream_t stream) {
+  switch (mode) {
+    case kSparse: return launch_one<D, BK, NQG, kSparse>(p, stream);
+    case kDense: return launch_one<D, BK, NQG, kDense>(p, stream);
+    default: return launch_one<D, BK, NQG, kCausal>(p, stream);
+  }
 }
 
 template <int D, int NQG>
-hipError_t launch_geom(const AttnParams& p, int bk, bool dense, hipStream_t stream) {
-  if (bk == 64) return launch_mode<D, 64, NQG>(p, dense, stream);
-  return launch_mode<D, 128, NQG>(p, dense, stream);
+hipError_t launch_geom(const AttnParams& p, int bk, int mode, hipStream_t stream) {
+  if (bk == 64) return launch_mode<D, 64, NQG>(p, mode, stream);
+  return launch_mode<D, 128, NQG>(p, mode, stream);
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, bool dense,
+hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, int mode,
                             hipStream_t stream) {
   if (p.n_wg == 0) return hipSuccess;
+  if (mode != kSparse && mode != kDense && mode != kCausal) return hipErrorInvalidValue;
   // One workgroup per query block: 4 waves for 64 rows, 8 waves for 128 rows.
   if (head_dim == 128)
-    return block_q == 64 ? launch_geom<128, 2>(p, block_k, dense, stream)
-                         : launch_geom<128, 4>(p, block_k, dense, stream);
-  return block_q == 64 ? launch_geom<64, 2>(p, block_k, dense, stream)
-                       : launch_geom<64, 4>(p, block_k, dense, stream);
+    return block_q == 64 ? launch_geom<128, 2>(p, block_k, mode, stream)
+                         : launch_geom<128, 4>(p, block_k, mode, stream);
+  return block_q == 64 ? launch_geom<64, 2>(p, block_k, mode, stream)
+                       : launch_geom<64, 4>(p, block_k, mode, stream);
 }
 
 }  // namespace bsattn

@@ -25,6 +25,7 @@ struct AttnParams {
   int32_t n_forced;         // protected blocks holding a real key: [0, n_forced)
   int32_t n_cand;           // generation blocks holding a real key: [P, P + n_cand)
   int32_t idx_row_stride;
+  int32_t causal_off;       // causal mode: real keys - real query rows (bottom-right alignment)
   int32_t n_wg;             // workgroups in the grid: batch * hq * nq
   float scale_log2;         // softmax scale * log2(e)
 };
@@ -52,8 +53,12 @@ struct ScoreParams {
   int32_t n_prefix_blocks, n_forced, n_cand, keep, idx_row_stride;
 };
 
+// Attention modes: the listed blocks, every non-empty block, or every block
+// up to the causal limit with the diagonal masked.
+enum AttnMode : int { kSparse = 0, kDense = 1, kCausal = 2 };
+
 // Launchers (return the HIP error of the launch).
-hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, bool dense,
+hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int block_k, int mode,
                             hipStream_t stream);
 hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t stream);
 hipError_t launch_score_topk(const ScoreParams& p, int head_dim, int batch, hipStream_t stream);

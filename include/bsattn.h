@@ -142,6 +142,23 @@ attn_status attn_block_sparse_fwd(const attn_shape* shape, const void* q, const 
 attn_status attn_dense_fwd(const attn_shape* shape, const void* q, const void* k, const void* v,
                            void* out, float* lse, hipStream_t stream);
 
+/* Causal dense attention (diffusers cosmos_parallel.py, cosmos3_cp_attention:
+ * the understanding pathway attends to itself causally; mstar PR #927,
+ * automated review: the dense pass keeps the bottom-right causal alignment of
+ * the FA3 call).
+ *
+ * Same arguments and layout as attn_dense_fwd. Keys are ranked in order among
+ * the real keys only (the prefix segment's real keys, then the generation
+ * segment's); with n_k real keys and n_q = q_valid real rows, real row t
+ * attends the real keys of rank <= t + (n_k - n_q), so the last real row sees
+ * every real key (bottom-right alignment). For a stream attending to itself
+ * (n_k == n_q, e.g. kv_prefix_len = 0 and kv_suffix_valid = q_valid) this is
+ * the usual mask "key <= query". Rows left with no key (n_q > n_k) give 0 and
+ * lse -inf, as padded rows do. Blocks past a query block's last reachable key
+ * are not visited. */
+attn_status attn_dense_causal_fwd(const attn_shape* shape, const void* q, const void* k,
+                                  const void* v, void* out, float* lse, hipStream_t stream);
+
 /* Whether `shape` is supported by the sparse path, checked without touching
  * the device (vllm-omni PR #8335, Purpose: sparse compatibility is checked
  * independently of dense-kernel restrictions). ATTN_OK or the error the

@@ -305,6 +305,28 @@ def make_config(name: str, layer: int = 0, pad_fill=None) -> Case:
     return make_case(name, cfg=cfg, layer=layer, sparsity=sparsity, pad_fill=pad_fill, **c)
 
 
+def make_und_case(layer: int = 0, pad_fill=None, block: int = 128) -> Case:
+    """The understanding stream of layer ``layer`` of the two-stream schedule,
+    attending to itself causally: its 1,000 tokens padded to a block multiple
+    are both the query rows and the keys (no prefix segment). The keys and
+    values are the bytes of the two-stream case's prefix segment (same
+    seeds); the queries are drawn as segment 2."""
+    c = CONFIGS["twostream"]
+    cfg, und, hq, hkv, d = c["cfg"], c["prefix"], c["hq"], c["hkv"], c["d"]
+    lay = make_layout(1, hq, hkv, d, block, block, prefix=0, gen=und)
+    q = np.zeros((1, lay["q_len"], hq, d), dtype=np.uint16)
+    k = np.zeros((1, lay["kv_len"], hkv, d), dtype=np.uint16)
+    v = np.zeros((1, lay["kv_len"], hkv, d), dtype=np.uint16)
+    # key = (cfg, layer, stream, batch row, segment): segment 1 = the
+    # understanding tokens as keys/values, 2 = the understanding queries
+    q[0, :und] = _gen_rows((cfg, layer, STREAM_Q, 0, 2), und, hq, d)
+    k[0, :und] = _gen_rows((cfg, layer, STREAM_K, 0, 1), und, hkv, d)
+    v[0, :und] = _gen_rows((cfg, layer, STREAM_V, 0, 1), und, hkv, d)
+    case = Case("und_causal", lay, q, k, v, 0, dict(cfg=cfg, layer=layer, dist="normal"))
+    _fill_padding(case, pad_fill)
+    return case
+
+
 def sample_rows(case: Case, per_head: int, seed_layer: int = 0):
     """Query rows to check at full size: rows 0 and q_valid-1 plus uniform draws.
 

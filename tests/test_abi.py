@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_three_calls_and_helpers():
     names = _declared()
-    for n in ("attn_select_blocks", "attn_block_sparse_fwd", "attn_dense_fwd"):
+    for n in ("attn_select_blocks", "attn_block_sparse_fwd", "attn_dense_fwd",
+              "attn_dense_causal_fwd"):
         assert n in names
     assert set(names) == set(bsa.EXPORTS)
 
@@ -125,6 +126,9 @@ def test_attention_argument_errors():
     assert L.attn_dense_fwd(_shape(), FAKE, FAKE, FAKE, FAKE,
                             ctypes.c_void_p((1 << 40) + 2), None) == 1
     assert L.attn_dense_fwd(_shape(block_q=48), FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert L.attn_dense_causal_fwd(_shape(), FAKE, None, FAKE, FAKE, None, None) == 1
+    assert L.attn_dense_causal_fwd(_shape(head_dim=96), FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert "attn_dense_causal_fwd" in bsa.last_error()
     s = bsa.make_shape(_layout())
     s.k_stride[1] = 260  # not a multiple of 8 elements
     assert L.attn_dense_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, None, None) == 2
