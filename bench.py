@@ -3,9 +3,11 @@ edge-video-shaped workload, one MI355X.
 
 One step = the whole hot path over synthetic inputs already in HBM: block
 selection (pooling + scores + top-k) followed by block-sparse attention
-(``edge48k``, ``video720p``); dense attention alone (``dense8k``); or the
-36-layer two-stream schedule, 8 dense layers then 28 selected-sparse layers
-(``twostream``). Prints one JSON line. ``value`` is effective attention
+(``edge48k``, ``video720p``); dense attention alone (``dense8k``); causal
+dense attention of the understanding stream over itself (``undcausal``); or
+the 36-layer two-stream schedule (``twostream``): per layer the understanding
+stream's causal self-attention, then the generation stream over cat(und, gen),
+dense for the first 8 layers and selected-sparse for the other 28. Prints one JSON line. ``value`` is effective attention
 TFLOP/s of the step (4 * block_q * block_k * head_dim FLOP per selected tile,
 selection time included in the denominator); the attention kernel alone is
 reported in ``roofline`` against the bf16 MFMA peak, timed with HIP events on
@@ -39,10 +41,13 @@ WORKLOAD_TEXT = {
     "dense8k": "dense GQA: batch 1, 32 query / 8 KV heads, head_dim 128, 8,192 tokens, 128x128 blocks",
     "video720p": ("720p-video-shaped sparse attention: 32/8 heads, head_dim 128, 512 prefix + "
                   "172,800 generation tokens (48x45x80), 128x128 blocks, 75% target (339 of 1354)"),
-    "twostream": ("two-stream schedule: generation stream of 20,000 tokens (padded to 20,096) "
-                  "attending to cat(understanding stream of 1,000 tokens padded to 1,024, "
-                  "generation stream), 32/8 heads, head_dim 128, 128x128 blocks, 36 layers with "
-                  "fresh inputs: 8 dense, then 28 at 75% target (42 of 165 blocks)"),
+    "twostream": ("two-stream schedule, 36 layers with fresh inputs, 32/8 heads, head_dim 128, "
+                  "128x128 blocks; per layer the understanding stream (1,000 tokens padded to "
+                  "1,024) attends to itself causally, then the generation stream (20,000 tokens "
+                  "padded to 20,096) attends to cat(understanding, generation): dense in layers "
+                  "0-7, 75% target (42 of 165 blocks) in layers 8-35"),
+    "undcausal": ("understanding-stream causal self-attention: 1,000 tokens padded to 1,024, "
+                  "32/8 heads, head_dim 128, 128x128 blocks, bottom-right causal mask"),
 }
 
 
@@ -86,6 +91,52 @@ def recorded_traffic(name):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def causal_tiles(lay):
+    """(query block, KV block) tiles the causal kernel visits per head: block
+    j is visited for query block i when its first real key's rank is within
+    reach of block i's last real row (rank <= row + n_k - n_q), and the count
+    of (real row, real key) pairs the causal mask keeps."""
+    bq, bk = lay["block_q"], lay["block_k"]
+    nq = lay["q_len"] // bq
+    pv, sv, pl = lay["kv_prefix_valid"], lay["kv_suffix_valid"], lay["kv_prefix_len"]
+    off = pv + sv - lay["q_valid"]
+    firsts = [j * bk for j in range((pv + bk - 1) // bk)] + \
+        [pv + m * bk for m in range((sv + bk - 1) // bk)]
+    tiles = 0
+    for i in range(nq):
+        if i * bq >= lay["q_valid"]:
+            continue
+        last = min((i + 1) * bq, lay["q_valid"]) - 1 + off
+        tiles += sum(1 for f in firsts if f <= last)
+    t = np.arange(lay["q_valid"])
+    pairs = int(np.clip(t + off + 1, 0, pv + sv).sum())
+    return tiles, pairs
+
+
+def cpu_baseline_causal(case):
+    """The fp64 oracle's causal dense attention, untouched, on the whole
+    understanding-stream case (every head); effective FLOPs of the visited
+    tiles, like the GPU figure."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    lay = case.layout
+    t0 = time.perf_counter()
+    oracle.dense_causal(lay, case.q, case.k, case.v)
+    t = time.perf_counter() - t0
+    tiles, _ = causal_tiles(lay)
+    flops = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * tiles * lay["batch"] * \
+        lay["num_q_heads"]
+    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    return {
+        "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"understanding stream layer {case.meta.get('layer', 0)}, all "
+                   f"{lay['num_q_heads']} query heads, fp64 causal attention ({t:.2f} s); "
+                   "effective FLOPs of the visited tiles"),
+        "seconds": round(t, 2),
+    }
 
 
 def cpu_baseline(case, keep, n_blocks):
@@ -148,13 +199,26 @@ def main():
     torch.cuda.set_device(dev)
     name = args.workload
     schedule = name == "twostream"
-    n_sets = synth.CONFIGS[name]["layers"] if schedule else max(1, args.input_sets)
-    sets = []
+    und_only = name == "undcausal"
+    n_sets = synth.CONFIGS["twostream"]["layers"] if schedule else max(1, args.input_sets)
+
+    def gpu(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets, und_sets = [], []
     for layer in range(n_sets):
-        case = synth.make_config(name, layer=layer)
-        t = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-             for a in (case.q, case.k, case.v)]
+        if und_only:
+            case = synth.make_und_case(layer)
+        else:
+            case = synth.make_config(name, layer=layer)
+        t = [gpu(a) for a in (case.q, case.k, case.v)]
         sets.append((case, t))
+        if schedule:
+            # The understanding stream's keys and values are the first segment
+            # of this layer's K/V (views, no copy); its queries are its own.
+            uc = synth.make_und_case(layer)
+            ul = uc.layout["kv_len"]
+            und_sets.append((uc, [gpu(uc.q), t[1][:, :ul], t[2][:, :ul]]))
         print(f"bench: input set {layer} of {name} ready", file=sys.stderr, flush=True)
     case0 = sets[0][0]
     lay = case0.layout
@@ -166,33 +230,48 @@ def main():
     cnt = torch.empty((b, hq, nq), dtype=torch.int32, device=dev)
     ws = torch.empty(max(bsa.select_workspace_size(lay), 256), dtype=torch.uint8, device=dev)
     outs = [torch.empty_like(t[0]) for _, t in sets]
+    und_outs = [torch.empty_like(t[0]) for _, t in und_sets]
     stream = torch.cuda.current_stream()
 
-    # One step: a list of (input set, dense?) layer calls.
+    # One step: a list of layer calls (input set, kind); kind is "sparse"
+    # (selection + block-sparse attention), "dense", "causal" (the measured
+    # kernel is the causal one) or "und" (the understanding stream's causal
+    # attention inside the two-stream schedule, timed on its own).
     if schedule:
-        plan = [[(s, sets[s][0].sparsity == 0) for s in range(len(sets))]]
+        plan = [[c for s in range(len(sets))
+                 for c in ((s, "und"), (s, "dense" if sets[s][0].sparsity == 0 else "sparse"))]]
+    elif und_only:
+        plan = [[(s, "causal")] for s in range(len(sets))]
     else:
-        plan = [[(s, case0.sparsity == 0)] for s in range(len(sets))]
+        plan = [[(s, "dense" if case0.sparsity == 0 else "sparse")] for s in range(len(sets))]
 
-    def layer_call(s, dense, ev=None):
+    def layer_call(s, kind, ev=None):
+        if kind == "und":
+            uc, (q, k, v) = und_sets[s]
+            if ev is not None:
+                ev[3].record(stream)
+            bsa.dense_attention(q, k, v, uc.layout, causal=True, out=und_outs[s], stream=stream)
+            if ev is not None:
+                ev[4].record(stream)
+            return
         _, (q, k, v) = sets[s]
         if ev is not None:
             ev[0].record(stream)
-        if not dense:
+        if kind == "sparse":
             bsa.select_blocks(q, k, lay, keep, keep, block_idx=idx, block_cnt=cnt, workspace=ws,
                               stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        if dense:
-            bsa.dense_attention(q, k, v, lay, out=outs[s], stream=stream)
-        else:
+        if kind == "sparse":
             bsa.block_sparse_attention(q, k, v, idx, cnt, lay, out=outs[s], stream=stream)
+        else:
+            bsa.dense_attention(q, k, v, lay, causal=kind == "causal", out=outs[s], stream=stream)
         if ev is not None:
             ev[2].record(stream)
 
     def step(i, evs=None):
-        for j, (s, dense) in enumerate(plan[i % len(plan)]):
-            layer_call(s, dense, None if evs is None else evs[j])
+        for j, (s, kind) in enumerate(plan[i % len(plan)]):
+            layer_call(s, kind, None if evs is None else evs[j])
 
     if args.calibrate_copy > 0:
         src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
@@ -205,13 +284,20 @@ def main():
     # work of each step from the counts the selector actually produced.
     tile_flops = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"]
     real_rows = (torch.arange(nq, device=dev) * lay["block_q"] < lay["q_valid"])
-    step_flops = []
+    step_flops, und_flops = [], 0.0
     for i in range(len(plan)):
         f = 0.0
-        for s, dense in plan[i]:
-            layer_call(s, dense)
-            if dense:
+        for s, kind in plan[i]:
+            layer_call(s, kind)
+            if kind == "dense":
                 f += tile_flops * b * hq * nq * nk
+            elif kind in ("causal", "und"):
+                ul = (und_sets[s][0] if kind == "und" else sets[s][0]).layout
+                tf = 4.0 * ul["block_q"] * ul["block_k"] * ul["head_dim"]
+                fc = tf * causal_tiles(ul)[0] * ul["batch"] * ul["num_q_heads"]
+                f += fc
+                if kind == "und":
+                    und_flops += fc
             else:
                 torch.cuda.synchronize()
                 if not bool((cnt[:, :, real_rows] == keep).all()):
@@ -223,7 +309,7 @@ def main():
     torch.cuda.synchronize()
 
     n_calls = len(plan[0])
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_calls)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_calls)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -231,19 +317,25 @@ def main():
         step(i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sel_ms = [sum(e[0].elapsed_time(e[1]) for e in ev) for ev in events]
-    att_ms = [sum(e[1].elapsed_time(e[2]) for e in ev) for ev in events]
+    kinds = [kind for _, kind in plan[0]]
+    main_calls = [j for j, kind in enumerate(kinds) if kind != "und"]
+    und_calls = [j for j, kind in enumerate(kinds) if kind == "und"]
+    sel_ms = [sum(ev[j][0].elapsed_time(ev[j][1]) for j in main_calls) for ev in events]
+    att_ms = [sum(ev[j][1].elapsed_time(ev[j][2]) for j in main_calls) for ev in events]
+    und_ms = [sum(ev[j][3].elapsed_time(ev[j][4]) for j in und_calls) for ev in events]
     eff_flops = float(np.mean([step_flops[i % len(plan)] for i in range(args.steps)]))
     ms_per_step = wall * 1e3 / args.steps
     att_avg = float(np.mean(att_ms))
-    att_tflops = eff_flops / (att_avg * 1e-3) / 1e12
+    # the roofline covers the main attention launches; the understanding
+    # stream's causal launches of the schedule are reported beside it
+    att_tflops = (eff_flops - und_flops) / (att_avg * 1e-3) / 1e12
     value = eff_flops / (ms_per_step * 1e-3) / 1e12
+    n_main = len(main_calls)
 
-    dense_only = all(d for call in plan for _, d in call)
-    kname = f"attn_fwd_kernel<{lay['head_dim']},{lay['block_q']},{lay['block_k']}," \
-        f"{'dense' if dense_only else 'sparse'}>"
+    mode = "causal" if und_only else ("dense" if all(k == "dense" for k in kinds) else "sparse")
+    kname = f"attn_fwd_kernel<{lay['head_dim']},{lay['block_q']},{lay['block_k']},{mode}>"
     if schedule:
-        kname += " (8 dense + 28 sparse launches per step)"
+        kname += " (8 dense + 28 sparse generation-stream launches per step)"
     traffic = recorded_traffic(name)
     result = {
         "metric": "effective attention TFLOP/s + ms/call at 75% sparsity, 48k tokens, 1 MI355X",
@@ -264,10 +356,13 @@ def main():
                    "block": f"{lay['block_q']}x{lay['block_k']}", "kv_blocks": nk,
                    "kept_blocks": keep, "sparsity_pct": sparse_case.sparsity if sparse_case else 0,
                    "input_sets": len(sets), "calls_per_step": n_calls},
-        "attn_ms_per_call": round(att_avg / n_calls, 4),
+        "und_causal_ms_per_step": round(float(np.mean(und_ms)), 4) if und_calls else None,
+        "und_causal_tflops": (round(und_flops / (float(np.mean(und_ms)) * 1e-3) / 1e12, 2)
+                              if und_calls else None),
+        "attn_ms_per_call": round(att_avg / n_main, 4),
         "attn_ms_per_step": round(att_avg, 4),
-        "attn_ms_median": round(float(np.median(att_ms)) / n_calls, 4),
-        "attn_ms_min": round(float(np.min(att_ms)) / n_calls, 4),
+        "attn_ms_median": round(float(np.median(att_ms)) / n_main, 4),
+        "attn_ms_min": round(float(np.min(att_ms)) / n_main, 4),
         "attn_tflops": round(att_tflops, 2),
         "select_ms_per_step": round(float(np.mean(sel_ms)), 4),
         "effective_tflop_per_step": round(eff_flops / 1e12, 4),
@@ -282,10 +377,17 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if und_only:
+        tiles, pairs = causal_tiles(lay)
+        result["config"]["causal_tiles_per_head"] = tiles
+        result["config"]["causal_pairs_per_head"] = pairs
     if not args.no_cpu_baseline:
-        cb_case = sparse_case if sparse_case is not None else case0
-        result["cpu_baseline"] = cpu_baseline(cb_case, keep if sparse_case is not None else None,
-                                              args.cpu_sample_blocks)
+        if und_only:
+            result["cpu_baseline"] = cpu_baseline_causal(case0)
+        else:
+            cb_case = sparse_case if sparse_case is not None else case0
+            result["cpu_baseline"] = cpu_baseline(cb_case, keep if sparse_case is not None else None,
+                                                  args.cpu_sample_blocks)
     print(json.dumps(result), flush=True)
 
 
