@@ -46,6 +46,13 @@ WORKLOAD_TEXT = {
                   "1,024) attends to itself causally, then the generation stream (20,000 tokens "
                   "padded to 20,096) attends to cat(understanding, generation): dense in layers "
                   "0-7, 75% target (42 of 165 blocks) in layers 8-35"),
+    "edge48k_256x128": ("edge-video-shaped sparse attention with 256x128 blocks: 32/8 heads, "
+                        "head_dim 128, 512 prefix + 48,360 generation tokens (31x30x52) padded to "
+                        "48,384, 75% target (96 of 382 KV blocks per 256-row block)"),
+    "mha64_48k": ("edge-video-shaped sparse attention, MHA at head_dim 64: 32 query / 32 KV heads, "
+                  "512 prefix + 48,360 generation tokens, 64x64 blocks, 75% target (191 of 764)"),
+    "mqa48k": ("edge-video-shaped sparse attention, MQA: 32 query heads / 1 KV head, head_dim 128, "
+               "512 prefix + 48,360 generation tokens, 64x64 blocks, 75% target (191 of 764)"),
     "undcausal": ("understanding-stream causal self-attention: 1,000 tokens padded to 1,024, "
                   "32/8 heads, head_dim 128, 128x128 blocks, bottom-right causal mask"),
 }

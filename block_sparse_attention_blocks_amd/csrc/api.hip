@@ -45,6 +45,9 @@ attn_status ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Attention workgroups per query block: a workgroup covers at most 128 rows.
+int qparts_of(const attn_shape* s) { return s->block_q > 128 ? s->block_q / 128 : 1; }
+
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Everything about the shape that the kernels rely on.
@@ -60,10 +63,11 @@ attn_status validate_shape(const attn_shape* s, const char* fn) {
   if (s->head_dim != 64 && s->head_dim != 128)
     return fail(ATTN_ERR_UNSUPPORTED, fn, "head_dim %d unsupported (supported: 64, 128)",
                 s->head_dim);
-  if ((s->block_q != 64 && s->block_q != 128) || (s->block_k != 64 && s->block_k != 128))
+  if ((s->block_q != 64 && s->block_q != 128 && s->block_q != 256) ||
+      (s->block_k != 64 && s->block_k != 128))
     return fail(ATTN_ERR_UNSUPPORTED, fn,
-                "block geometry %dx%d unsupported (block_q and block_k in {64, 128})", s->block_q,
-                s->block_k);
+                "block geometry %dx%d unsupported (block_q in {64, 128, 256}, block_k in {64, 128})",
+                s->block_q, s->block_k);
   if (s->q_len < 0 || s->q_len % s->block_q != 0)
     return fail(ATTN_ERR_INVALID_ARG, fn, "q_len %d is not a non-negative multiple of block_q %d",
                 s->q_len, s->block_q);
@@ -95,7 +99,7 @@ attn_status validate_shape(const attn_shape* s, const char* fn) {
     return fail(ATTN_ERR_INVALID_ARG, fn, "softmax_scale is not finite");
   if (s->batch > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, fn, "batch %d > 65535", s->batch);
-  const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / s->block_q);
+  const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / s->block_q) * qparts_of(s);
   if (nwg > 0x7FFFFFFF) return fail(ATTN_ERR_UNSUPPORTED, fn, "grid too large");
   return ATTN_OK;
 }
@@ -223,7 +227,8 @@ attn_status run_attention(const char* fn, const attn_shape* s, const void* q, co
   p.n_cand = d.n_cand;
   p.idx_row_stride = dense ? 0 : idx_row_stride;
   p.causal_off = (s->kv_prefix_valid + s->kv_suffix_valid) - s->q_valid;
-  p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq);
+  p.qparts = qparts_of(s);
+  p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq * p.qparts);
   p.scale_log2 = scale_of(s) * 1.4426950408889634f;
   if (p.n_wg == 0) return ok();
   st = check_device(fn);

@@ -196,12 +196,15 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int half = lane >> 5;
 
   // Workgroup w runs on XCD w % 8; give each XCD a contiguous range of the
-  // (batch, KV head, query block, head-in-group) order.
+  // (batch, KV head, query block, head-in-group, part) order. A query block
+  // of more than 128 rows is split into parts of 32 NQG rows, one workgroup
+  // each, reading the same list (neighbours in this order share an XCD).
   const int nwg = p.n_wg;
   const int w = blockIdx.x;
   const int xcd = w & 7, per = nwg >> 3, rem = nwg & 7;
   const int lin = xcd * per + min(xcd, rem) + (w >> 3);
-  int t = lin;
+  const int part = lin % p.qparts;
+  int t = lin / p.qparts;
   const int hig = t % p.group;
   t /= p.group;
   const int i = t % p.nq;
@@ -209,7 +212,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int g = t % p.hkv;
   const int b = t / p.hkv;
   const int h = g * p.group + hig;
-  const int row0 = i * (32 * NQG);
+  const int row0 = (i * p.qparts + part) * (32 * NQG);
   const int qrow = row0 + 32 * qh + col;
 
   // Q^T fragments (B operand): the lane holds q[qrow][16 ks + 8 half .. +7].
@@ -626,7 +629,8 @@ hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int 
                             hipStream_t stream) {
   if (p.n_wg == 0) return hipSuccess;
   if (mode != kSparse && mode != kDense && mode != kCausal) return hipErrorInvalidValue;
-  // One workgroup per query block: 4 waves for 64 rows, 8 waves for 128 rows.
+  // One workgroup per query block: 4 waves for 64 rows, 8 waves for 128 rows;
+  // 256-row blocks run as two 128-row workgroups (p.qparts = 2).
   if (head_dim == 128)
     return block_q == 64 ? launch_geom<128, 2>(p, block_k, mode, stream)
                          : launch_geom<128, 4>(p, block_k, mode, stream);

@@ -26,7 +26,8 @@ struct AttnParams {
   int32_t n_cand;           // generation blocks holding a real key: [P, P + n_cand)
   int32_t idx_row_stride;
   int32_t causal_off;       // causal mode: real keys - real query rows (bottom-right alignment)
-  int32_t n_wg;             // workgroups in the grid: batch * hq * nq
+  int32_t qparts;           // workgroups per query block: block_q / 128 above 128 rows, else 1
+  int32_t n_wg;             // workgroups in the grid: batch * hq * nq * qparts
   float scale_log2;         // softmax scale * log2(e)
 };
 

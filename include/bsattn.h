@@ -64,7 +64,7 @@ typedef struct attn_shape {
   int32_t num_q_heads;   /* Hq >= 1 */
   int32_t num_kv_heads;  /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
   int32_t head_dim;      /* D in {64, 128} */
-  int32_t block_q;       /* query rows per block, in {64, 128} */
+  int32_t block_q;       /* query rows per block, in {64, 128, 256} */
   int32_t block_k;       /* keys per block, in {64, 128} */
   int32_t q_len;         /* padded query length, multiple of block_q */
   int32_t q_valid;       /* real query rows [0, q_valid) */

@@ -47,6 +47,15 @@ CONFIGS = {
                     frames=(31, 30, 52), bq=64, bk=64, sparsity=75, dist="lowrank"),
     "video720p": dict(cfg=4, batch=1, hq=32, hkv=8, d=128, prefix=512, gen=172800,
                       frames=(48, 45, 80), bq=128, bk=128, sparsity=75, dist="lowrank"),
+    # Other geometries and head layouts at the 48k edge-video token shape:
+    # 256x128 blocks (the pages' Blackwell validation geometry), MHA at
+    # head_dim 64, MQA.
+    "edge48k_256x128": dict(cfg=6, batch=1, hq=32, hkv=8, d=128, prefix=512, gen=48360,
+                            frames=(31, 30, 52), bq=256, bk=128, sparsity=75, dist="lowrank"),
+    "mha64_48k": dict(cfg=7, batch=1, hq=32, hkv=32, d=64, prefix=512, gen=48360,
+                      frames=(31, 30, 52), bq=64, bk=64, sparsity=75, dist="lowrank"),
+    "mqa48k": dict(cfg=8, batch=1, hq=32, hkv=1, d=128, prefix=512, gen=48360,
+                   frames=(31, 30, 52), bq=64, bk=64, sparsity=75, dist="lowrank"),
     # Two-stream schedule: 36 layers, layers < 8 dense, the rest 75 % sparse.
     "twostream": dict(cfg=5, batch=1, hq=32, hkv=8, d=128, prefix=1000, gen=20000,
                       bq=128, bk=128, sparsity=75, dist="normal",

@@ -66,6 +66,7 @@ def _layout(**kw):
     (dict(num_q_heads=3), 1),                   # Hq % Hkv != 0
     (dict(head_dim=96), 2),                     # unsupported head_dim
     (dict(block_q=32), 2),                      # unsupported geometry
+    (dict(block_q=512, q_len=512), 2),
     (dict(block_k=256), 2),
     (dict(q_len=250), 1),                       # not a block multiple
     (dict(q_valid=300), 1),                     # valid > len

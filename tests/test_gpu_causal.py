@@ -47,6 +47,8 @@ def _check(case, lay=None, what="causal"):
                              gen=700)),
     ("prefix_d64_64x128", dict(cfg=57, hq=2, hkv=1, d=64, bq=64, bk=128, prefix=64, gen=321)),
     ("one_token", dict(cfg=58, hq=2, hkv=1, d=64, bq=64, bk=64, prefix=0, gen=1)),
+    ("square_256x128", dict(cfg=62, hq=4, hkv=2, d=128, bq=256, bk=128, prefix=0, gen=1000)),
+    ("prefix_256x64_d64", dict(cfg=63, hq=2, hkv=1, d=64, bq=256, bk=64, prefix=100, gen=600)),
 ])
 def test_causal_shapes(name, kw):
     _check(synth.make_case(name, **kw))

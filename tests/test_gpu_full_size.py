@@ -86,6 +86,23 @@ def test_edge48k_bench_launch():
     _check_rows(case, out, lse, ridx, rcnt, 256, what="sparse")
 
 
+@pytest.mark.parametrize("name,keep_expected", [
+    ("edge48k_256x128", 96), ("mha64_48k", 191), ("mqa48k", 191)])
+def test_other_geometries_at_48k(name, keep_expected):
+    """256x128 blocks, MHA at head_dim 64 and MQA at the 48k token shape:
+    full selection bit-exact, sampled rows of every head."""
+    case = synth.make_config(name)
+    lay = case.layout
+    nq, nk, p = bsa.num_blocks(lay)
+    keep = bsa.keep_blocks(nk, p, case.sparsity)
+    assert keep == keep_expected
+    note(f"[gpu] {name} {lay} keep={keep}")
+    (q, k, v, idx, cnt, stream), (ridx, rcnt) = _select_and_compare(case, keep)
+    out, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, return_lse=True, stream=stream)
+    torch.cuda.synchronize()
+    _check_rows(case, out, lse, ridx, rcnt, 64, what=name)
+
+
 def test_dense8k_full_size():
     case = synth.make_config("dense8k")
     lay = case.layout

@@ -70,6 +70,8 @@ def test_tiny_config():
     ("no_prefix", dict(hq=2, hkv=1, d=128, prefix=0, gen=500, cfg=46), 75),
     ("one_key", dict(hq=2, hkv=1, d=64, prefix=0, gen=1, cfg=47), 0),
     ("int_ties", dict(hq=2, hkv=1, d=64, prefix=64, gen=448, dist="int", int_range=1, cfg=48), 50),
+    ("bq256_bk128", dict(hq=4, hkv=2, d=128, bq=256, bk=128, prefix=130, gen=1100, cfg=49), 75),
+    ("bq256_bk64_d64", dict(hq=2, hkv=1, d=64, bq=256, bk=64, prefix=64, gen=600, cfg=50), 50),
 ])
 def test_shapes_and_edges(name, kw, pct):
     _full_check(synth.make_case(name, **kw), pct, stride_extra=3)

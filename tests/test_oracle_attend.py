@@ -52,6 +52,7 @@ def _sdpa_masked(case, idx, cnt):
     ("gqa_ragged", dict(hq=4, hkv=2, d=64, prefix=100, gen=300, cfg=21)),
     ("mqa_bq128", dict(hq=3, hkv=1, d=64, bq=128, bk=64, prefix=0, gen=500, cfg=22)),
     ("lowrank", dict(hq=4, hkv=1, d=128, prefix=64, gen=480, frames=(1, 20, 24), dist="lowrank", cfg=23)),
+    ("bq256_bk128", dict(hq=2, hkv=1, d=64, bq=256, bk=128, prefix=128, gen=600, cfg=24)),
 ])
 def test_sparse_attend_equals_sdpa_with_block_mask(name, kw):
     case = synth.make_config("tiny") if name == "tiny" else synth.make_case(**kw)
