@@ -15,7 +15,9 @@ What it computes, step by step, in the order of the method:
                       padded keys excluded, GQA head h -> KV head h // G;
 * ``dense``         - the same with every block selected;
 * ``dense_causal``  - causal dense attention, bottom-right aligned over the
-                      real tokens (the understanding pathway's self-attention).
+                      real tokens (the understanding pathway's self-attention);
+* ``strategy``      - which attention a (denoising step, layer) call runs
+                      under a dense-then-sparse strategy, and that call.
 
 Sources (web pages): vllm-omni PR #8335 "[Core] Add shared block-sparse
 attention adapters with FlashAttention-4" (Purpose: selector producing
@@ -27,7 +29,8 @@ keys masked; ``cosmos3_cp_attention``: the generation pathway attends with full
 attention to cat(und, gen)); mstar PR #927 (automated review: default softmax
 scale head_dim**-0.5; bottom-right causal alignment of the dense pass);
 ``cosmos3_cp_attention`` again for the understanding pathway's causal
-self-attention.
+self-attention; vllm-omni PR #8583 (Purpose, Test Result) and PR #8644
+(Purpose) for the step/layer strategy.
 
 Parity: every function here is pinned by CPU tests against closed forms,
 brute force, exact rational arithmetic and torch's fp64 SDPA; none is
@@ -36,9 +39,10 @@ brute force, exact rational arithmetic and torch's fp64 SDPA; none is
 from .selector import keep_blocks, valid_key_mask, valid_query_mask, pool, block_scores, \
     select, select_from_scores, rn32_exact, widen_bf16
 from .attention import attend, attend_rows, dense, dense_causal, identity_selection, key_ranks
+from . import strategy
 
 __all__ = [
     "keep_blocks", "valid_key_mask", "valid_query_mask", "pool", "block_scores", "select",
     "select_from_scores", "rn32_exact", "widen_bf16", "attend", "attend_rows", "dense",
-    "dense_causal", "identity_selection", "key_ranks",
+    "dense_causal", "identity_selection", "key_ranks", "strategy",
 ]
