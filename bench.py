@@ -245,8 +245,19 @@ def main():
     # kernel is the causal one) or "und" (the understanding stream's causal
     # attention inside the two-stream schedule, timed on its own).
     if schedule:
-        plan = [[c for s in range(len(sets))
-                 for c in ((s, "und"), (s, "dense" if sets[s][0].sparsity == 0 else "sparse"))]]
+        # The library's step/layer strategy decides each generation-stream
+        # call: the Cosmos3 mixed recipe (10 dense steps, then layers 8-35
+        # sparse) at its first sparse step.
+        tc = synth.CONFIGS["twostream"]
+        strategy = bsa.make_strategy(tc["layers"], 10, range(tc["dense_layers"], tc["layers"]),
+                                     tc["sparsity"])
+        kinds = ["sparse" if bsa.strategy_is_sparse(strategy, 10, s) else "dense"
+                 for s in range(len(sets))]
+        if any((kd == "dense") != (sets[s][0].sparsity == 0) for s, kd in enumerate(kinds)):
+            raise RuntimeError("strategy decisions disagree with the schedule's inputs")
+        _, (q0, k0, v0) = sets[0]
+        bsa.strategy_warmup(q0, k0, v0, lay, strategy, out=outs[0])
+        plan = [[c for s in range(len(sets)) for c in ((s, "und"), (s, kinds[s]))]]
     elif und_only:
         plan = [[(s, "causal")] for s in range(len(sets))]
     else:

@@ -46,9 +46,17 @@ class AttnShape(ctypes.Structure):
     ]
 
 
+class AttnStrategy(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32), ("dense_steps", ctypes.c_int32),
+        ("sparse_layers", ctypes.c_uint64), ("sparsity_pct", ctypes.c_int32),
+    ]
+
+
 EXPORTS = ("attn_keep_blocks", "attn_select_workspace_size", "attn_select_blocks",
            "attn_block_sparse_fwd", "attn_dense_fwd", "attn_dense_causal_fwd",
-           "attn_query_support", "attn_last_error", "attn_version")
+           "attn_strategy_is_sparse", "attn_strategy_workspace_size", "attn_strategy_fwd",
+           "attn_strategy_warmup", "attn_query_support", "attn_last_error", "attn_version")
 
 
 def _load():
@@ -71,6 +79,15 @@ def _load():
     lib.attn_dense_fwd.restype = I32
     lib.attn_dense_causal_fwd.argtypes = [SH, P, P, P, P, P, P]
     lib.attn_dense_causal_fwd.restype = I32
+    ST = ctypes.POINTER(AttnStrategy)
+    lib.attn_strategy_is_sparse.argtypes = [ST, I32, I32]
+    lib.attn_strategy_is_sparse.restype = I32
+    lib.attn_strategy_workspace_size.argtypes = [SH, ST]
+    lib.attn_strategy_workspace_size.restype = SZ
+    lib.attn_strategy_fwd.argtypes = [SH, ST, I32, I32, P, P, P, P, P, P, SZ, P]
+    lib.attn_strategy_fwd.restype = I32
+    lib.attn_strategy_warmup.argtypes = [SH, ST, P, P, P, P, P, SZ, P]
+    lib.attn_strategy_warmup.restype = I32
     lib.attn_query_support.argtypes = [SH]
     lib.attn_query_support.restype = I32
     lib.attn_last_error.argtypes = []
@@ -241,6 +258,73 @@ def dense_attention(q, k, v, layout, *, causal=False, out=None, return_lse=False
     return (out, lse) if return_lse else out
 
 
+def make_strategy(num_layers: int, dense_steps: int, sparse_layers, sparsity_pct: int) -> AttnStrategy:
+    """attn_strategy: steps [0, dense_steps) dense in every layer, then the
+    layers in ``sparse_layers`` sparse at ``sparsity_pct``."""
+    mask = 0
+    for layer in sparse_layers:
+        if not 0 <= int(layer) < 64:
+            raise ValueError("layers must be in [0, 64)")
+        mask |= 1 << int(layer)
+    return AttnStrategy(int(num_layers), int(dense_steps), mask, int(sparsity_pct))
+
+
+def strategy_is_sparse(strategy: AttnStrategy, step: int, layer: int) -> bool:
+    r = lib.attn_strategy_is_sparse(ctypes.byref(strategy), int(step), int(layer))
+    if r < 0:
+        raise ValueError("invalid strategy or (step, layer)")
+    return bool(r)
+
+
+def strategy_workspace_size(layout, strategy: AttnStrategy) -> int:
+    n = lib.attn_strategy_workspace_size(ctypes.byref(make_shape(layout)), ctypes.byref(strategy))
+    if n == 0:
+        raise ValueError("invalid layout or strategy")
+    return n
+
+
+def _strategy_ws(layout, strategy, workspace, device):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(strategy_workspace_size(layout, strategy), dtype=torch.uint8,
+                                device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def strategy_forward(q, k, v, layout, strategy: AttnStrategy, step: int, layer: int, *, out=None,
+                     return_lse=False, workspace=None, stream=None):
+    """The attention of (step, layer) under ``strategy`` (attn_strategy_fwd):
+    dense, or selection + block-sparse attention."""
+    import torch
+    _check_tensor(q, "q", torch.bfloat16)
+    for t, n in ((k, "k"), (v, "v")):
+        _check_tensor(t, n, torch.bfloat16, q.device)
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    lse = None
+    if return_lse:
+        lse = torch.empty((int(layout["batch"]), int(layout["num_q_heads"]), int(layout["q_len"])),
+                          dtype=torch.float32, device=q.device)
+    ws, nbytes = _strategy_ws(layout, strategy, workspace, q.device)
+    shape = make_shape(layout, q=q, k=k, v=v, out=out)
+    _check(lib.attn_strategy_fwd(ctypes.byref(shape), ctypes.byref(strategy), int(step), int(layer),
+                                 _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws), nbytes,
+                                 _stream_handle(stream)))
+    return (out, lse) if return_lse else out
+
+
+def strategy_warmup(q, k, v, layout, strategy: AttnStrategy, *, out=None, workspace=None,
+                    stream=None):
+    """Run every kind of call the strategy makes once (attn_strategy_warmup)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(q, memory_format=torch.contiguous_format)
+    ws, nbytes = _strategy_ws(layout, strategy, workspace, q.device)
+    shape = make_shape(layout, q=q, k=k, v=v, out=out)
+    _check(lib.attn_strategy_warmup(ctypes.byref(shape), ctypes.byref(strategy), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(out), _ptr(ws), nbytes, _stream_handle(stream)))
+
+
 def query_support(layout):
     """(status, message) of attn_query_support for a layout."""
     st = lib.attn_query_support(ctypes.byref(make_shape(layout)))
@@ -275,6 +359,8 @@ def pad_segments(q_gen, k_prefix, v_prefix, k_gen, v_gen, block_q: int, block_k:
     return q, k, v, layout
 
 
-__all__ = ["BsAttnError", "AttnShape", "EXPORTS", "LIB_PATH", "lib", "version", "last_error",
-           "make_shape", "keep_blocks", "num_blocks", "select_workspace_size", "select_blocks",
-           "block_sparse_attention", "dense_attention", "query_support", "pad_segments"]
+__all__ = ["BsAttnError", "AttnShape", "AttnStrategy", "EXPORTS", "LIB_PATH", "lib", "version",
+           "last_error", "make_shape", "keep_blocks", "num_blocks", "select_workspace_size",
+           "select_blocks", "block_sparse_attention", "dense_attention", "make_strategy",
+           "strategy_is_sparse", "strategy_workspace_size", "strategy_forward",
+           "strategy_warmup", "query_support", "pad_segments"]

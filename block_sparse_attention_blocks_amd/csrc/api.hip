@@ -366,6 +366,104 @@ attn_status attn_query_support(const attn_shape* s) {
   return ok();
 }
 
+// ------------------------------------------------------------- strategy
+int32_t attn_strategy_is_sparse(const attn_strategy* st, int32_t step, int32_t layer) {
+  if (st == nullptr || st->num_layers < 1 || st->num_layers > 64 || st->dense_steps < 0 ||
+      st->sparsity_pct < 0 || st->sparsity_pct > 100 || step < 0 || layer < 0 ||
+      layer >= st->num_layers)
+    return -1;
+  if (st->num_layers < 64 && (st->sparse_layers >> st->num_layers) != 0) return -1;
+  if (step < st->dense_steps) return 0;
+  return (int32_t)((st->sparse_layers >> layer) & 1u);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of a strategy call: block lists, counts, then the selector's.
+struct StrategyWs {
+  int32_t keep;
+  size_t idx, cnt, sel, total;
+};
+
+bool strategy_ws(const attn_shape* s, const attn_strategy* st, StrategyWs* w) {
+  if (validate_shape(s, "attn_strategy") != ATTN_OK) return false;
+  if (attn_strategy_is_sparse(st, 0, 0) < 0) return false;
+  const Derived d = derive(s);
+  w->keep = attn_keep_blocks(d.nk, d.P, st->sparsity_pct);
+  if (w->keep < 0) return false;
+  const size_t rows = (size_t)s->batch * s->num_q_heads * d.nq;
+  w->idx = 0;
+  w->cnt = round256(rows * (size_t)(w->keep > 0 ? w->keep : 1) * sizeof(int32_t));
+  w->sel = w->cnt + round256(rows * sizeof(int32_t));
+  w->total = w->sel + ws_layout(s).total;
+  return true;
+}
+
+attn_status strategy_call(const char* fn, const attn_shape* s, const attn_strategy* st,
+                          bool sparse, const void* q, const void* k, const void* v, void* out,
+                          float* lse, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!sparse) return attn_dense_fwd(s, q, k, v, out, lse, stream);
+  StrategyWs w;
+  if (!strategy_ws(s, st, &w)) return fail(ATTN_ERR_INVALID_ARG, fn, "invalid shape or strategy");
+  if (workspace == nullptr || workspace_bytes < w.total)
+    return fail(ATTN_ERR_WORKSPACE, fn, "workspace %zu bytes < %zu required", workspace_bytes,
+                w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(ATTN_ERR_WORKSPACE, fn, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = reinterpret_cast<int32_t*>(ws + w.idx);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + w.cnt);
+  const int32_t stride = w.keep > 0 ? w.keep : 1;
+  attn_status r = attn_select_blocks(s, q, k, w.keep, idx, cnt, stride, ws + w.sel,
+                                     workspace_bytes - w.sel, stream);
+  if (r != ATTN_OK) return r;
+  return attn_block_sparse_fwd(s, q, k, v, idx, cnt, stride, out, lse, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_strategy_workspace_size(const attn_shape* s, const attn_strategy* st) {
+  StrategyWs w;
+  return strategy_ws(s, st, &w) ? w.total : 0;
+}
+
+attn_status attn_strategy_fwd(const attn_shape* s, const attn_strategy* st, int32_t step,
+                              int32_t layer, const void* q, const void* k, const void* v,
+                              void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  const char* fn = "attn_strategy_fwd";
+  const int32_t sp = attn_strategy_is_sparse(st, step, layer);
+  if (sp < 0)
+    return fail(ATTN_ERR_INVALID_ARG, fn, "invalid strategy or (step %d, layer %d)", step, layer);
+  return strategy_call(fn, s, st, sp == 1, q, k, v, out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_strategy_warmup(const attn_shape* s, const attn_strategy* st, const void* q,
+                                 const void* k, const void* v, void* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "attn_strategy_warmup";
+  if (attn_strategy_is_sparse(st, 0, 0) < 0) return fail(ATTN_ERR_INVALID_ARG, fn, "invalid strategy");
+  const uint64_t all = st->num_layers == 64 ? ~0ull : ((1ull << st->num_layers) - 1);
+  const bool any_dense = st->dense_steps > 0 || (st->sparse_layers & all) != all;
+  const bool any_sparse = st->sparse_layers != 0;
+  if (any_dense) {
+    const attn_status r =
+        strategy_call(fn, s, st, false, q, k, v, out, nullptr, workspace, workspace_bytes, stream);
+    if (r != ATTN_OK) return r;
+  }
+  if (any_sparse) {
+    const attn_status r =
+        strategy_call(fn, s, st, true, q, k, v, out, nullptr, workspace, workspace_bytes, stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ok();
+}
+
 const char* attn_last_error(void) { return t_last_error.c_str(); }
 
 const char* attn_version(void) { return BSATTN_VERSION; }

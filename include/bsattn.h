@@ -159,6 +159,54 @@ attn_status attn_dense_fwd(const attn_shape* shape, const void* q, const void* k
 attn_status attn_dense_causal_fwd(const attn_shape* shape, const void* q, const void* k,
                                   const void* v, void* out, float* lse, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Step/layer attention strategy: a thin host layer over the calls above that
+ * picks dense or selected-sparse attention per (denoising step, layer)
+ * (vllm-omni PR #8583, Purpose: dense/sparse switch by step and layer, a
+ * uniform dense-to-sparse switch and a mixed-layer policy, warmup across
+ * layouts; PR #8644, Purpose: the first twenty iterations dense, then every
+ * layer sparse).
+ *
+ * Steps [0, dense_steps) run every layer dense. From step dense_steps on,
+ * layer l runs sparse when bit l of sparse_layers is set, dense otherwise.
+ * Examples: the Cosmos3 mixed recipe is {36, 10, bits 8..35, 75}; always
+ * sparse is {36, 0, all 36 bits, 75}; the H3 switch is {50, 20, all 50 bits,
+ * 75}. */
+typedef struct attn_strategy {
+  int32_t num_layers;     /* layers per denoising step, 1..64 */
+  int32_t dense_steps;    /* >= 0 */
+  uint64_t sparse_layers; /* bit l = layer l sparse after dense_steps; no bit at or above num_layers */
+  int32_t sparsity_pct;   /* target sparsity of the sparse calls, 0..100 (attn_keep_blocks) */
+} attn_strategy;
+
+/* 1 if the call of `layer` in denoising step `step` is sparse, 0 if dense,
+ * -1 if the strategy or (step, layer) is invalid. Pure host arithmetic. */
+int32_t attn_strategy_is_sparse(const attn_strategy* strategy, int32_t step, int32_t layer);
+
+/* Bytes of device workspace attn_strategy_fwd and attn_strategy_warmup need
+ * for `shape`: the block lists and counts of a sparse call followed by the
+ * selector's workspace. 0 if the shape or the strategy is invalid. */
+size_t attn_strategy_workspace_size(const attn_shape* shape, const attn_strategy* strategy);
+
+/* The attention of (step, layer) under `strategy`: attn_dense_fwd for a dense
+ * call; for a sparse call attn_select_blocks with keep_blocks =
+ * attn_keep_blocks(NK, P, sparsity_pct) into the workspace, then
+ * attn_block_sparse_fwd. Arguments as for those calls; the workspace
+ * (256-byte aligned, attn_strategy_workspace_size bytes) is scratch owned by
+ * the caller. Errors of the underlying calls propagate unchanged. */
+attn_status attn_strategy_fwd(const attn_shape* shape, const attn_strategy* strategy,
+                              int32_t step, int32_t layer, const void* q, const void* k,
+                              const void* v, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Warmup across layouts: runs once every kind of call the strategy can make
+ * for `shape` (dense and/or select + sparse), so the first launch of each
+ * kernel (which loads its code object) happens before the first denoising
+ * step. `out` is overwritten; the workspace is as for attn_strategy_fwd. */
+attn_status attn_strategy_warmup(const attn_shape* shape, const attn_strategy* strategy,
+                                 const void* q, const void* k, const void* v, void* out,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Whether `shape` is supported by the sparse path, checked without touching
  * the device (vllm-omni PR #8335, Purpose: sparse compatibility is checked
  * independently of dense-kernel restrictions). ATTN_OK or the error the

@@ -154,3 +154,52 @@ def test_binding_fails_loudly_without_library(tmp_path):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def _golden_recipes():
+    import json
+    from conftest import GOLDEN
+    return json.load(open(os.path.join(GOLDEN, "strategy_recipes.json")))["recipes"]
+
+
+def test_strategy_decisions_match_the_oracle():
+    """attn_strategy_is_sparse (host arithmetic) against the oracle's
+    strategy on every (step, layer) of the pages' recipes."""
+    import oracle
+    for r in _golden_recipes():
+        spec = r["sparse_layers"]
+        layers = list(range(int(spec.split("-")[0]), int(spec.split("-")[1]) + 1)) if spec else []
+        st = bsa.make_strategy(r["num_layers"], r["dense_steps"], layers, 75)
+        got = [bsa.strategy_is_sparse(st, s, l) for s in range(r["steps"])
+               for l in range(r["num_layers"])]
+        ref = [oracle.strategy.is_sparse(r["num_layers"], r["dense_steps"], layers, s, l)
+               for s in range(r["steps"]) for l in range(r["num_layers"])]
+        assert got == ref
+        assert sum(got) == r["sparse_calls"]
+
+
+def test_strategy_validation_and_workspace():
+    L = bsa.lib
+    ok = bsa.make_strategy(36, 10, range(8, 36), 75)
+    assert L.attn_strategy_is_sparse(ctypes.byref(ok), 0, 36) == -1
+    assert L.attn_strategy_is_sparse(ctypes.byref(ok), -1, 0) == -1
+    bad = bsa.AttnStrategy(36, 10, 1 << 40, 75)            # a layer bit past num_layers
+    assert L.attn_strategy_is_sparse(ctypes.byref(bad), 12, 0) == -1
+    assert L.attn_strategy_is_sparse(ctypes.byref(bsa.AttnStrategy(0, 0, 0, 75)), 0, 0) == -1
+    assert L.attn_strategy_is_sparse(ctypes.byref(bsa.AttnStrategy(4, 0, 1, 101)), 0, 0) == -1
+    assert L.attn_strategy_is_sparse(None, 0, 0) == -1
+    lay = _layout()
+    n = bsa.strategy_workspace_size(lay, ok)
+    nq, nk, p = bsa.num_blocks(lay)
+    keep = bsa.keep_blocks(nk, p, 75)
+    rows = lay["batch"] * lay["num_q_heads"] * nq
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert n == r256(rows * keep * 4) + r256(rows * 4) + bsa.select_workspace_size(lay)
+    assert L.attn_strategy_workspace_size(_shape(head_dim=80), ctypes.byref(ok)) == 0
+    assert L.attn_strategy_workspace_size(_shape(), ctypes.byref(bad)) == 0
+    # a sparse call with too small a workspace fails on the host
+    assert L.attn_strategy_fwd(_shape(), ctypes.byref(ok), 12, 9, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, n - 1, None) == 3
+    assert L.attn_strategy_fwd(_shape(), ctypes.byref(ok), 0, 40, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, n, None) == 1
+    assert "attn_strategy_fwd" in bsa.last_error()
