@@ -104,48 +104,54 @@ __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
 // ------------------------------------------------------- exact dot product
 // Exact sum of D products of fp32 pairs in a 576-bit two's complement fixed
 // point accumulator (bit 0 weighs 2^-298, below the smallest product
-// 2^-149 * 2^-149), then rounded to the nearest fp32, ties to even.
-// a: D values (fp32 held exactly in fp64), b: D fp32 values at stride bstride.
-__device__ __noinline__ float exact_dot_rn32(const double* a, const float* b, int64_t bstride,
-                                             int D) {
-  constexpr int NL = 9;
-  uint64_t acc[NL];
+// 2^-149 * 2^-149; the largest sum stays below 2^561), then rounded to the
+// nearest fp32, ties to even. A whole wave computes one sum: lane l adds the
+// products l, l + 64, ... into its own accumulator, and a butterfly over the
+// lanes adds the accumulators (additions modulo 2^576 are exact).
+constexpr int kLimbs = 9;
+
+// acc += the exact product of the fp32 values with bit patterns ua and ub.
+__device__ __forceinline__ void acc_add_product(uint64_t (&acc)[kLimbs], uint32_t ua, uint32_t ub) {
+  const uint32_t ea = (ua >> 23) & 0xFFu, eb = (ub >> 23) & 0xFFu;
+  const uint64_t ma = (ua & 0x7FFFFFu) | (ea ? 0x800000u : 0u);
+  const uint64_t mb = (ub & 0x7FFFFFu) | (eb ? 0x800000u : 0u);
+  const uint64_t m = ma * mb;  // < 2^48
+  if (m == 0) return;
+  const int xa = ea ? (int)ea - 150 : -149;
+  const int xb = eb ? (int)eb - 150 : -149;
+  const int pos = xa + xb + 298;  // in [0, 506]
+  const int limb = pos >> 6, off = pos & 63;
+  const uint64_t lo = m << off;
+  const uint64_t hi = off ? (m >> (64 - off)) : 0;
+  const bool neg = ((ua ^ ub) >> 31) != 0;
+  // acc += (neg ? -X : X), X = lo * 2^(64 limb) + hi * 2^(64 (limb + 1)); -X = ~X + 1.
+  uint64_t carry = neg ? 1 : 0;
 #pragma unroll
-  for (int L = 0; L < NL; ++L) acc[L] = 0;
-  for (int d = 0; d < D; ++d) {
-    const uint32_t ua = __float_as_uint((float)a[d]);
-    const uint32_t ub = __float_as_uint(b[(int64_t)d * bstride]);
-    const uint32_t ea = (ua >> 23) & 0xFFu, eb = (ub >> 23) & 0xFFu;
-    const uint64_t ma = (ua & 0x7FFFFFu) | (ea ? 0x800000u : 0u);
-    const uint64_t mb = (ub & 0x7FFFFFu) | (eb ? 0x800000u : 0u);
-    const uint64_t m = ma * mb;  // < 2^48
-    if (m == 0) continue;
-    const int xa = ea ? (int)ea - 150 : -149;
-    const int xb = eb ? (int)eb - 150 : -149;
-    const int pos = xa + xb + 298;  // in [0, 506]
-    const int limb = pos >> 6, off = pos & 63;
-    const uint64_t lo = m << off;
-    const uint64_t hi = off ? (m >> (64 - off)) : 0;
-    const bool neg = ((ua ^ ub) >> 31) != 0;
-    // acc += (neg ? -X : X), X = lo * 2^(64 limb) + hi * 2^(64 (limb + 1)); -X = ~X + 1.
-    uint64_t carry = neg ? 1 : 0;
-#pragma unroll
-    for (int L = 0; L < NL; ++L) {
-      uint64_t x = (L == limb) ? lo : ((L == limb + 1) ? hi : 0);
-      if (neg) x = ~x;
-      const uint64_t s1 = acc[L] + x;
-      const uint64_t c1 = s1 < x;
-      const uint64_t s2 = s1 + carry;
-      const uint64_t c2 = s2 < carry;
-      acc[L] = s2;
-      carry = c1 | c2;
-    }
+  for (int L = 0; L < kLimbs; ++L) {
+    uint64_t x = (L == limb) ? lo : ((L == limb + 1) ? hi : 0);
+    if (neg) x = ~x;
+    const uint64_t s1 = acc[L] + x;
+    const uint64_t c1 = s1 < x;
+    const uint64_t s2 = s1 + carry;
+    const uint64_t c2 = s2 < carry;
+    acc[L] = s2;
+    carry = c1 | c2;
   }
-  const bool negr = (acc[NL - 1] >> 63) != 0;
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const int lo = __shfl_xor((int)(uint32_t)v, mask);
+  const int hi = __shfl_xor((int)(uint32_t)(v >> 32), mask);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Nearest fp32 (ties to even) of the fixed-point value.
+__device__ __forceinline__ float acc_round_rn32(uint64_t (&acc)[kLimbs]) {
+  const bool negr = (acc[kLimbs - 1] >> 63) != 0;
   if (negr) {  // magnitude
     uint64_t carry = 1;
 #pragma unroll
-    for (int L = 0; L < NL; ++L) {
+    for (int L = 0; L < kLimbs; ++L) {
       const uint64_t x = ~acc[L];
       const uint64_t s = x + carry;
       carry = s < carry;
@@ -154,7 +160,7 @@ __device__ __noinline__ float exact_dot_rn32(const double* a, const float* b, in
   }
   int top = -1;  // highest set bit
 #pragma unroll
-  for (int L = NL - 1; L >= 0; --L)
+  for (int L = kLimbs - 1; L >= 0; --L)
     if (top < 0 && acc[L] != 0) top = 64 * L + 63 - __clzll(acc[L]);
   if (top < 0) return 0.0f;  // exact zero: +0
   const int etop = top - 298;
@@ -165,7 +171,7 @@ __device__ __noinline__ float exact_dot_rn32(const double* a, const float* b, in
   uint64_t w0 = 0, w1 = 0;
   bool sticky = false;
 #pragma unroll
-  for (int L = 0; L < NL; ++L) {
+  for (int L = 0; L < kLimbs; ++L) {
     if (L == wl) {
       w0 = acc[L];
       sticky = sticky || (wo ? (acc[L] & ((1ull << wo) - 1)) != 0 : false);
@@ -180,6 +186,37 @@ __device__ __noinline__ float exact_dot_rn32(const double* a, const float* b, in
   const float mag = (float)__builtin_ldexp((double)mant, lsb - 298);  // exact in fp32
   return negr ? -mag : mag;
 }
+
+// a: D values (fp32 held exactly in fp64), b: D fp32 values at stride
+// bstride. Called by a whole wave with uniform arguments; every lane returns
+// the result.
+__device__ __noinline__ float exact_dot_rn32_wave(const double* a, const float* b, int64_t bstride,
+                                                  int D, int lane) {
+  uint64_t acc[kLimbs];
+#pragma unroll
+  for (int L = 0; L < kLimbs; ++L) acc[L] = 0;
+  for (int d = lane; d < D; d += 64)
+    acc_add_product(acc, __float_as_uint((float)a[d]), __float_as_uint(b[(int64_t)d * bstride]));
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) {
+    uint64_t carry = 0;
+#pragma unroll
+    for (int L = 0; L < kLimbs; ++L) {
+      const uint64_t x = shfl_xor_u64(acc[L], sh);
+      const uint64_t s1 = acc[L] + x;
+      const uint64_t c1 = s1 < x;
+      const uint64_t s2 = s1 + carry;
+      const uint64_t c2 = s2 < carry;
+      acc[L] = s2;
+      carry = c1 | c2;
+    }
+  }
+  return acc_round_rn32(acc);
+}
+
+// Key of a score whose fp32 rounding the fp64 bound leaves open; above every
+// key of a finite score.
+constexpr uint32_t kUndecided = 0xFFFFFFFFu;
 
 // Monotone map of fp32 values to unsigned keys (-0 and +0 map alike).
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -247,12 +284,28 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
           const double w = gamma2 * qnorm[r] * knj + __builtin_fabs(sc) * 0x1p-52;
           const float lo = (float)(sc - w);
           const float hi = (float)(sc + w);
-          float f = lo;
-          if (__float_as_uint(lo) != __float_as_uint(hi))
-            f = exact_dot_rn32(qrows + (int64_t)r * D, kcols + j, p.nk, D);
-          keys_lds[r * ncp + c] = order_key(f);
+          // Undecided roundings are marked and recomputed exactly below, out
+          // of this loop (finite scores never map to the marker).
+          keys_lds[r * ncp + c] =
+              __float_as_uint(lo) != __float_as_uint(hi) ? kUndecided : order_key(lo);
         }
       }
+    }
+  }
+  __syncthreads();
+  // Exact recomputation of the marked scores (rare: a few in a hundred
+  // thousand for typical inputs, but any number is handled), one whole wave
+  // per score.
+  for (int e0 = wave * 64; e0 < nrows * ncp; e0 += 256) {
+    const int e = e0 + lane;
+    uint64_t marked = __builtin_amdgcn_ballot_w64(e < nrows * ncp && keys_lds[e] == kUndecided);
+    while (marked != 0) {
+      const int ee = e0 + (int)__builtin_ctzll(marked);
+      marked &= marked - 1;
+      const int r = ee / ncp, c = ee % ncp;
+      const float f = exact_dot_rn32_wave(qrows + (int64_t)r * D, kcols + p.n_prefix_blocks + c,
+                                          p.nk, D, lane);
+      if (lane == 0) keys_lds[ee] = order_key(f);
     }
   }
   __syncthreads();
