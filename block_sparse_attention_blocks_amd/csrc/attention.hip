@@ -412,10 +412,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     // ---- the step's single synchronisation point.
     wait_vmcnt<0>();
     lds_barrier();
+    // Past the end of the list the copies still run (their slots are never
+    // read again, or only by the masked dummy product) but read this head's
+    // first rows, which are always in bounds: no branch per copy.
     const bool v_next = u + 1 < nst, k_next = u + 2 < nst;
     const uint16_t* v_rows =
-        vbase + copy_row_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) * p.vs1;
-    const uint16_t* k_rows = kbase + copy_row_of((SPB == 1) ? j2 : j1, u + 2) * p.ks1;
+        v_next ? vbase + copy_row_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) * p.vs1
+               : vbase + (int64_t)wave * RPW * p.vs1;
+    const uint16_t* k_rows =
+        k_next ? kbase + copy_row_of((SPB == 1) ? j2 : j1, u + 2) * p.ks1
+               : kbase + (int64_t)wave * RPW * p.ks1;
     const uint16_t* kb = smem + KP * STAGE;
     uint16_t* vb = smem + (2 + VP) * STAGE;
     const int nvs = nvs_of(nv0, u);
@@ -458,9 +464,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       if (k % CEVERY == 0) {
         const int c = k / CEVERY;
         if (c < Copy::NL) {
-          if (v_next) vcopy.issue_one(c, v_rows, v_stage(VP ^ 1));
+          vcopy.issue_one(c, v_rows, v_stage(VP ^ 1));
         } else {
-          if (k_next) kcopy.issue_one(c - Copy::NL, k_rows, k_stage(KP ^ 1));
+          kcopy.issue_one(c - Copy::NL, k_rows, k_stage(KP ^ 1));
         }
       }
 #pragma unroll
@@ -530,6 +536,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const float ltot = sum_with_other_half(lsum);
   constexpr int HT = DT / 2;   // output tiles finished per wave
   constexpr int XR = HT * 16;  // accumulator registers handed over
+  wait_vmcnt<0>();  // the last steps' copies land before the LDS is reused
   lds_barrier();
   float* xo = reinterpret_cast<float*>(smem) + wave * (XR + 2) * 64;
   const float* yo = reinterpret_cast<const float*>(smem) + (wave ^ 1) * (XR + 2) * 64;
