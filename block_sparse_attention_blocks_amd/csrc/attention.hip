@@ -19,7 +19,8 @@
 // block's rows. Each wave keeps its own partial softmax state; the two key
 // halves are merged once at the end. A wave needs fewer than 256 registers,
 // so every SIMD runs two waves (two 4-wave workgroups per CU at 64-row
-// blocks, one 8-wave workgroup at 128-row blocks): while one wave waits (LDS,
+// blocks, one 8-wave workgroup at 128-row blocks; a 256-row block runs as two
+// 128-row workgroups on the same list): while one wave waits (LDS,
 // barrier, the HBM copies) the other issues, and one wave's softmax overlaps
 // the other's matrix products.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K fragment (A operand)
@@ -40,7 +41,8 @@
 //  * K and V stages move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
 //    staging), XOR-swizzled in 16-byte chunks so that the K row reads and
 //    the V transpose reads hit distinct banks, double buffered: K two stages
-//    ahead, V one. One workgroup barrier per stage.
+//    ahead, V one. One workgroup barrier per stage. Past the end of the list
+//    the copies keep running on in-bounds rows, so they need no branch.
 //  * Workgroups are renumbered so that each XCD works through a contiguous
 //    range of (KV head, query block), keeping that range's K/V tiles in the
 //    XCD's L2.
