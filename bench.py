@@ -67,7 +67,10 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3,
                     help="distinct input sets rotated over the steps (twostream: always its 36 layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=756)
+    ap.add_argument("--cpu-sample-blocks", type=int, default=756,
+                    help="query blocks per sampled head in the CPU baseline")
+    ap.add_argument("--cpu-sample-heads", type=int, default=3,
+                    help="query heads sampled in the CPU baseline (about 4 s of oracle work each at 48k)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -146,46 +149,52 @@ def cpu_baseline_causal(case):
     }
 
 
-def cpu_baseline(case, keep, n_blocks):
+def cpu_baseline(case, keep, n_blocks, n_heads):
     """The fp64 oracle, untouched, on a bounded sample of the same workload:
-    selection for query head 0 (all its query blocks; skipped for a dense
-    layer, ``keep`` None) and attention for the first ``n_blocks`` query
-    blocks of that head. Reported as effective TFLOP/s of the sampled blocks,
-    the selection time pro-rated to them."""
+    for each of the first ``n_heads`` query heads, selection over all its
+    query blocks (skipped for a dense layer, ``keep`` None) and attention for
+    its first ``n_blocks`` query blocks. Reported as effective TFLOP/s of the
+    sampled blocks, the selection time pro-rated to them."""
     import oracle
     from threadpoolctl import threadpool_info
 
     lay = case.layout
     hq, hkv = lay["num_q_heads"], lay["num_kv_heads"]
-    g = 0
-    lay1 = dict(lay, num_q_heads=1, num_kv_heads=1)
-    q1 = np.ascontiguousarray(case.q[:, :, 0:1])
-    k1 = np.ascontiguousarray(case.k[:, :, g:g + 1])
-    v1 = np.ascontiguousarray(case.v[:, :, g:g + 1])
-    t0 = time.perf_counter()
-    if keep is None:
-        idx, cnt = oracle.identity_selection(lay1)
-    else:
-        idx, cnt = oracle.select(lay1, q1, k1, keep)
-    t_sel = time.perf_counter() - t0 if keep is not None else 0.0
+    grp = hq // hkv
+    n_heads = max(1, min(n_heads, hq))
     nq = lay["q_len"] // lay["block_q"]
     n_blocks = min(n_blocks, nq)
-    idx_s = idx[:, :, :n_blocks]
-    cnt_s = cnt[:, :, :n_blocks]
-    lay_s = dict(lay1, q_len=n_blocks * lay["block_q"], q_valid=min(lay["q_valid"], n_blocks * lay["block_q"]))
-    t0 = time.perf_counter()
-    oracle.attend(lay_s, q1[:, :lay_s["q_len"]], k1, v1, idx_s, cnt_s)
-    t_att = time.perf_counter() - t0
-    flops = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * float(cnt_s.sum())
+    lay1 = dict(lay, num_q_heads=1, num_kv_heads=1)
+    lay_s = dict(lay1, q_len=n_blocks * lay["block_q"],
+                 q_valid=min(lay["q_valid"], n_blocks * lay["block_q"]))
+    t_sel = t_att = flops = 0.0
+    for h in range(n_heads):
+        g = h // grp
+        q1 = np.ascontiguousarray(case.q[:, :, h:h + 1])
+        k1 = np.ascontiguousarray(case.k[:, :, g:g + 1])
+        v1 = np.ascontiguousarray(case.v[:, :, g:g + 1])
+        t0 = time.perf_counter()
+        if keep is None:
+            idx, cnt = oracle.identity_selection(lay1)
+        else:
+            idx, cnt = oracle.select(lay1, q1, k1, keep)
+        if keep is not None:
+            t_sel += time.perf_counter() - t0
+        idx_s = idx[:, :, :n_blocks]
+        cnt_s = cnt[:, :, :n_blocks]
+        t0 = time.perf_counter()
+        oracle.attend(lay_s, q1[:, :lay_s["q_len"]], k1, v1, idx_s, cnt_s)
+        t_att += time.perf_counter() - t0
+        flops += 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * float(cnt_s.sum())
     t = t_sel * n_blocks / nq + t_att
     threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     what = "dense (no selection)" if keep is None else f"selection over all {nq} query blocks " \
         f"({t_sel:.2f} s, pro-rated)"
     return {
         "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"{case.name} layer {case.meta.get('layer', 0)}, query head 0 of {hq}: {what}"
-                   f" + fp64 attention for {n_blocks} query blocks ({t_att:.2f} s); effective "
-                   "FLOPs of those blocks"),
+        "sample": (f"{case.name} layer {case.meta.get('layer', 0)}, query heads 0-{n_heads - 1} of "
+                   f"{hq}: {what} + fp64 attention for {n_blocks} query blocks per head "
+                   f"({t_att:.2f} s); effective FLOPs of those blocks"),
         "seconds": round(t_sel + t_att, 2),
     }
 
@@ -405,7 +414,7 @@ def main():
         else:
             cb_case = sparse_case if sparse_case is not None else case0
             result["cpu_baseline"] = cpu_baseline(cb_case, keep if sparse_case is not None else None,
-                                                  args.cpu_sample_blocks)
+                                                  args.cpu_sample_blocks, args.cpu_sample_heads)
     print(json.dumps(result), flush=True)
 
 
