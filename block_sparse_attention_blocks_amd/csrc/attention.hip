@@ -253,6 +253,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   }
   if (row0 >= p.q_valid || p.nk == 0) nblk = 0;
   const int nst = nblk * SPB;  // stages
+  // Where in its list this workgroup starts (it wraps around to the start).
+  // With two workgroups per CU the dispatcher settles into rounds of 64 per
+  // XCD whose second 32 start about half a workgroup lifetime after the
+  // first 32 (measured). Starting those at the middle of their lists keeps
+  // all the XCD's workgroups at about the same place in the KV sequence at
+  // any time, so they share the blocks in L2. The order depends on blockIdx
+  // only, so results stay bitwise reproducible.
+  const int n_first = (NQG == 2 && ((w >> 3) & 32)) ? nblk / 2 : 0;
 
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
@@ -268,7 +276,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 
   // Listed block n. Entries outside [0, NK) are copied from block 0 (always
   // in bounds) with no real key, which gives them zero weight.
-  auto block_of = [&](int n) -> int {
+  auto block_of = [&](int n_pos) -> int {
+    int n = n_pos + n_first;
+    if (n >= nblk) n -= nblk;
     if constexpr (DENSE) {
       return n < p.n_forced ? n : p.n_prefix_blocks + (n - p.n_forced);
     } else {
