@@ -100,7 +100,9 @@ attn_status validate_shape(const attn_shape* s, const char* fn) {
   if (s->batch > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, fn, "batch %d > 65535", s->batch);
   const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / s->block_q) * qparts_of(s);
-  if (nwg > 0x7FFFFFFF) return fail(ATTN_ERR_UNSUPPORTED, fn, "grid too large");
+  // (+ up to 7 padding workgroups per (batch, KV head) in the head-synchronous order)
+  if (nwg + 8 * (int64_t)s->batch * s->num_kv_heads > 0x7FFFFFFF)
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "grid too large");
   return ATTN_OK;
 }
 
@@ -229,6 +231,11 @@ attn_status run_attention(const char* fn, const attn_shape* s, const void* q, co
   p.causal_off = (s->kv_prefix_valid + s->kv_suffix_valid) - s->q_valid;
   p.qparts = qparts_of(s);
   p.n_wg = (int)((int64_t)s->batch * s->num_q_heads * d.nq * p.qparts);
+  // K and V of every (batch, KV head) together larger than the 256 MB
+  // last-level cache: let the XCDs work through the KV heads in step.
+  const int64_t kv_bytes =
+      (int64_t)s->batch * s->num_kv_heads * (int64_t)s->kv_len * s->head_dim * 2 * 2;
+  p.head_sync = kv_bytes > ((int64_t)256 << 20) ? 1 : 0;
   p.scale_log2 = scale_of(s) * 1.4426950408889634f;
   if (p.n_wg == 0) return ok();
   st = check_device(fn);

@@ -197,22 +197,37 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // Workgroup w runs on XCD w % 8; give each XCD a contiguous range of the
-  // (batch, KV head, query block, head-in-group, part) order. A query block
-  // of more than 128 rows is split into parts of 32 NQG rows, one workgroup
-  // each, reading the same list (neighbours in this order share an XCD).
-  const int nwg = p.n_wg;
+  // Workgroup w runs on XCD w % 8. The work is the (batch, KV head, query
+  // block, head-in-group, part) order; a query block of more than 128 rows
+  // is split into parts of 32 NQG rows, one workgroup each, reading the same
+  // list. Each XCD takes a contiguous range of that order, so neighbours
+  // (the heads of a group, adjacent query blocks: similar lists) share its
+  // L2. When the K/V of all heads would not fit in the 256 MB last-level
+  // cache together, the XCDs instead split every (batch, KV head) eight ways
+  // and move through the KV heads in step, so only one head's K/V is live;
+  // the grid is then padded to a multiple of eight per (batch, KV head).
   const int w = blockIdx.x;
-  const int xcd = w & 7, per = nwg >> 3, rem = nwg & 7;
-  const int lin = xcd * per + min(xcd, rem) + (w >> 3);
+  const int xcd = w & 7, kx = w >> 3;
+  int lin, bg;
+  if (p.head_sync) {
+    const int tot = p.nq * p.group * p.qparts;  // workgroups per (batch, KV head)
+    const int per = (tot + 7) >> 3;
+    bg = kx / per;
+    lin = xcd * per + kx % per;
+    if (lin >= tot) return;  // padding: the whole workgroup leaves before any barrier
+  } else {
+    const int nwg = p.n_wg, per = nwg >> 3, rem = nwg & 7;
+    const int all = xcd * per + min(xcd, rem) + kx;
+    const int tot = p.nq * p.group * p.qparts;
+    bg = all / tot;
+    lin = all % tot;
+  }
   const int part = lin % p.qparts;
   int t = lin / p.qparts;
   const int hig = t % p.group;
-  t /= p.group;
-  const int i = t % p.nq;
-  t /= p.nq;
-  const int g = t % p.hkv;
-  const int b = t / p.hkv;
+  const int i = t / p.group;
+  const int g = bg % p.hkv;
+  const int b = bg / p.hkv;
   const int h = g * p.group + hig;
   const int row0 = (i * p.qparts + part) * (32 * NQG);
   const int qrow = row0 + 32 * qh + col;
@@ -622,8 +637,10 @@ attn_fwd_kernel(const AttnParams p) {
 
 template <int D, int BK, int NQG, int MODE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, MODE>), dim3(p.n_wg), dim3(128 * NQG), 0,
-                     stream, p);
+  const int grid =
+      p.head_sync ? p.batch * p.hkv * 8 * ((p.nq * p.group * p.qparts + 7) / 8) : p.n_wg;
+  hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, MODE>), dim3(grid), dim3(128 * NQG), 0, stream,
+                     p);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ struct AttnParams {
   int32_t idx_row_stride;
   int32_t causal_off;       // causal mode: real keys - real query rows (bottom-right alignment)
   int32_t qparts;           // workgroups per query block: block_q / 128 above 128 rows, else 1
-  int32_t n_wg;             // workgroups in the grid: batch * hq * nq * qparts
+  int32_t n_wg;             // workgroups with work: batch * hq * nq * qparts
+  int32_t head_sync;        // 1: all XCDs on one KV head at a time (grid padded per head)
   float scale_log2;         // softmax scale * log2(e)
 };
 
