@@ -24,13 +24,18 @@ namespace bsattn {
 namespace {
 
 // ---------------------------------------------------------------- pooling
-// One workgroup per (batch, block) covers every head of that block: the
-// block's rows are contiguous [rows][heads][D] bf16, so the reads stream.
+// One workgroup per (batch, block, group of 2048 / D heads): thread t owns one
+// 16-byte chunk of one head's row and walks the block's rows. The rows are
+// [rows][heads][D] bf16, so the workgroup's reads stream; eight rows are in
+// flight per thread. Each chunk is summed over the rows in row order, in
+// fp64 (exact for these inputs).
 template <int D>
 __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
-  constexpr int CPH = D / 8;  // 16-byte chunks per head row
+  constexpr int CPH = D / 8;      // 16-byte chunks per head row
+  constexpr int HPW = 256 / CPH;  // heads per workgroup
   const int blk = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = blockIdx.z;
+  const int h0 = blockIdx.y * HPW;
   const bool isq = blk < p.nq;
   const int j = isq ? blk : blk - p.nq;
   const int heads = isq ? p.hq : p.hkv;
@@ -48,20 +53,20 @@ __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
   const uint16_t* base = isq ? p.q + (int64_t)b * p.qs0 : p.k + (int64_t)b * p.ks0;
   const int64_t s1 = isq ? p.qs1 : p.ks1;
   const int64_t s2 = isq ? p.qs2 : p.ks2;
-  const int nchunks = heads * CPH;
   const int nblocks = isq ? p.nq : p.nk;
+  if (h0 >= heads) return;  // the K blocks need fewer head groups than the Q blocks
 
-  for (int c0 = 0; c0 < nchunks; c0 += 256) {
-    const int c = c0 + (int)threadIdx.x;
-    const bool act = c < nchunks;
-    const int hh = act ? c / CPH : 0;
+  {
+    const int c = (int)threadIdx.x;
+    const bool act = h0 + c / CPH < heads;
+    const int hh = act ? h0 + c / CPH : h0;
     const int dc = c % CPH;
     double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0;
     if (act && n > 0) {
       const uint16_t* src = base + (int64_t)start * s1 + (int64_t)hh * s2 + dc * 8;
-#pragma unroll 4
+#pragma unroll 8
       for (int t = 0; t < n; ++t) {
         const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)t * s1);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -404,7 +409,9 @@ size_t score_lds_bytes(int n_cand) {
 }
 
 hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t stream) {
-  const dim3 grid(p.nq + p.nk, batch);
+  const int hpw = 256 / (head_dim / 8);
+  const int hmax = p.hq > p.hkv ? p.hq : p.hkv;
+  const dim3 grid(p.nq + p.nk, (hmax + hpw - 1) / hpw, batch);
   if (grid.x == 0) return hipSuccess;
   if (head_dim == 128)
     hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, stream, p);
