@@ -219,6 +219,13 @@ __device__ __noinline__ float exact_dot_rn32_wave(const double* a, const float* 
   return acc_round_rn32(acc);
 }
 
+// Minimum over the wave's 64 lanes (every lane gets it).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int sh = 1; sh < 64; sh <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, sh));
+  return v;
+}
+
 // Key of a score whose fp32 rounding the fp64 bound leaves open; above every
 // key of a finite score.
 constexpr uint32_t kUndecided = 0xFFFFFFFFu;
@@ -347,7 +354,17 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
 #pragma unroll
             for (int m = 0; m < 16; ++m)
               if (m < M) count += __popcll(__ballot(kreg[m] >= cand));
-            if (count >= rsel) thr = cand;
+            if (count == rsel) {
+              // Exactly the rsel largest keys are >= cand: the threshold is
+              // the smallest of them.
+              uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+              for (int m = 0; m < 16; ++m)
+                if (m < M && kreg[m] >= cand) mn = min(mn, kreg[m]);
+              thr = wave_min_u32(mn);
+              break;
+            }
+            if (count > rsel) thr = cand;
           }
           int gt = 0;
 #pragma unroll
@@ -362,7 +379,16 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
               const int jj = m * 64 + lane;
               count += __popcll(__ballot(jj < ncand && kr[jj] >= cand));
             }
-            if (count >= rsel) thr = cand;
+            if (count == rsel) {
+              uint32_t mn = 0xFFFFFFFFu;
+              for (int m = 0; m < M; ++m) {
+                const int jj = m * 64 + lane;
+                if (jj < ncand && kr[jj] >= cand) mn = min(mn, kr[jj]);
+              }
+              thr = wave_min_u32(mn);
+              break;
+            }
+            if (count > rsel) thr = cand;
           }
           int gt = 0;
           for (int m = 0; m < M; ++m) {
