@@ -103,6 +103,47 @@ def recorded_traffic(name):
         return None
 
 
+class SclkSampler:
+    """Samples the GPU's current shader clock (the starred level of the
+    driver's sysfs table) from a thread while the timed steps run; reports
+    the highest value seen, or None where the table is not readable."""
+
+    def __init__(self, period_s=0.02):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.seen = []
+        self.done = threading.Event()
+        self.thread = threading.Thread(target=self._run, args=(period_s,), daemon=True)
+        if self.path:
+            self.thread.start()
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self, period_s):
+        while not self.done.is_set():
+            v = self._read()
+            if v is not None:
+                self.seen.append(v)
+            self.done.wait(period_s)
+
+    def stop(self):
+        if not self.path:
+            return None
+        self.done.set()
+        self.thread.join(timeout=1.0)
+        return max(self.seen) if self.seen else None
+
+
 def causal_tiles(lay):
     """(query block, KV block) tiles the causal kernel visits per head: block
     j is visited for query block i when its first real key's rank is within
@@ -339,11 +380,13 @@ def main():
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_calls)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
+    clock = SclkSampler()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk = clock.stop()
     kinds = [kind for _, kind in plan[0]]
     main_calls = [j for j, kind in enumerate(kinds) if kind != "und"]
     und_calls = [j for j, kind in enumerate(kinds) if kind == "und"]
@@ -392,6 +435,7 @@ def main():
         "attn_ms_min": round(float(np.min(att_ms)) / n_main, 4),
         "attn_tflops": round(att_tflops, 2),
         "select_ms_per_step": round(float(np.mean(sel_ms)), 4),
+        "gpu_sclk_mhz_max_seen": sclk,
         "effective_tflop_per_step": round(eff_flops / 1e12, 4),
         "roofline": {
             "kernel": kname,
