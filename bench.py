@@ -436,6 +436,9 @@ def main():
         "attn_tflops": round(att_tflops, 2),
         "select_ms_per_step": round(float(np.mean(sel_ms)), 4),
         "gpu_sclk_mhz_max_seen": sclk,
+        # the bf16 MFMA peak scales with the shader clock (4096 FLOP per CU per cycle)
+        "attn_frac_of_peak_at_seen_clock": (round(att_tflops / (256 * 4096 * sclk * 1e6 / 1e12), 4)
+                                            if sclk else None),
         "effective_tflop_per_step": round(eff_flops / 1e12, 4),
         "roofline": {
             "kernel": kname,
