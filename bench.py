@@ -144,6 +144,30 @@ class SclkSampler:
         return max(self.seen) if self.seen else None
 
 
+def selector_bytes(lay, keep):
+    """Algorithmic bytes of one selection call: read Q and K once, write the
+    pooled vectors (queries fp64, keys fp32) and their norms, read them back
+    for the scores, write the lists and counts."""
+    b, hq, hkv, d = lay["batch"], lay["num_q_heads"], lay["num_kv_heads"], lay["head_dim"]
+    nq, nk = lay["q_len"] // lay["block_q"], lay["kv_len"] // lay["block_k"]
+    q = b * lay["q_len"] * hq * d * 2
+    k = b * lay["kv_len"] * hkv * d * 2
+    pooled = b * hq * nq * (d * 8 + 8) + b * hkv * nk * (d * 4 + 8)
+    lists = b * hq * nq * (keep + 1) * 4
+    return q + k + 2 * pooled + lists
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def causal_tiles(lay):
     """(query block, KV block) tiles the causal kernel visits per head: block
     j is visited for query block i when its first real key's rank is within
@@ -187,6 +211,7 @@ def cpu_baseline_causal(case):
                    f"{lay['num_q_heads']} query heads, fp64 causal attention ({t:.2f} s); "
                    "effective FLOPs of the visited tiles"),
         "seconds": round(t, 2),
+        "cpu_model": cpu_model(),
     }
 
 
@@ -237,6 +262,9 @@ def cpu_baseline(case, keep, n_blocks, n_heads):
                    f"{hq}: {what} + fp64 attention for {n_blocks} query blocks per head "
                    f"({t_att:.2f} s); effective FLOPs of those blocks"),
         "seconds": round(t_sel + t_att, 2),
+        "cpu_model": cpu_model(),
+        "select_seconds": round(t_sel, 2),
+        "attend_seconds": round(t_att, 2),
     }
 
 
@@ -435,6 +463,7 @@ def main():
         "attn_ms_min": round(float(np.min(att_ms)) / n_main, 4),
         "attn_tflops": round(att_tflops, 2),
         "select_ms_per_step": round(float(np.mean(sel_ms)), 4),
+        "selector": None,
         "gpu_sclk_mhz_max_seen": sclk,
         # the bf16 MFMA peak scales with the shader clock (4096 FLOP per CU per cycle)
         "attn_frac_of_peak_at_seen_clock": (round(att_tflops / (256 * 4096 * sclk * 1e6 / 1e12), 4)
@@ -451,6 +480,14 @@ def main():
         },
         "cpu_baseline": None,
     }
+    n_sel = sum(1 for _, kind in plan[0] if kind == "sparse")
+    if n_sel:
+        sel_call_ms = float(np.mean(sel_ms)) / n_sel
+        gbs = selector_bytes(lay, keep) / (sel_call_ms * 1e-3) / 1e9
+        result["selector"] = {"bound": "hbm", "ms_per_call": round(sel_call_ms, 4),
+                              "algorithmic_bytes": selector_bytes(lay, keep),
+                              "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                              "frac": round(gbs / 8000.0, 4)}
     if und_only:
         tiles, pairs = causal_tiles(lay)
         result["config"]["causal_tiles_per_head"] = tiles
