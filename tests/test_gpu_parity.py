@@ -189,6 +189,36 @@ def test_empty_and_degenerate_layouts():
     bsa.dense_attention(q, k, v, lay4, out=torch.empty_like(q))
 
 
+@pytest.mark.parametrize("bk,d", [(64, 64), (128, 128)])
+def test_selector_at_its_block_limit(bk, d):
+    """NK = 4096 KV blocks, the selector's limit (the 8-rows-per-workgroup
+    path with every key in LDS), and 75 % kept: full selection bit-exact,
+    attention over it against the oracle."""
+    nk = 4096
+    case = synth.make_case(f"nk4096_{bk}", cfg=90 + bk, hq=2, hkv=1, d=d, bq=64, bk=bk,
+                           prefix=2 * bk, gen=nk * bk - 2 * bk - 5)
+    lay = case.layout
+    assert lay["kv_len"] // bk == nk
+    # a few query blocks only: every block of the sequence stays a key
+    lay = dict(lay, q_len=256, q_valid=250)
+    q = case.q[:, :256].copy()
+    _, nkk, p = bsa.num_blocks(lay)
+    keep = bsa.keep_blocks(nkk, p, 75)
+    note(f"[gpu] selector at NK={nkk}, keep={keep}, bk={bk}, d={d}")
+    qg, kg, vg = case_to_gpu(synth.Case(case.name, lay, q, case.k, case.v, 75))
+    idx, cnt = bsa.select_blocks(qg, kg, lay, keep)
+    out = bsa.block_sparse_attention(qg, kg, vg, idx, cnt, lay)
+    torch.cuda.synchronize()
+    ridx, rcnt = oracle.select(lay, q, case.k, keep)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ro, _ = oracle.attend(lay, q, case.k, case.v, ridx, rcnt)
+    rows = _row_mask(lay)
+    g = out_to_f64(out)
+    assert_close(g[:, rows], ro[:, rows], what="nk4096")
+    assert (g[:, ~rows] == 0).all()
+
+
 def test_errors_propagate_from_the_binding():
     case = synth.make_config("tiny")
     q, k, v = case_to_gpu(case)
