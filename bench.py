@@ -106,9 +106,12 @@ def recorded_traffic(name):
 class SclkSampler:
     """Samples the GPU's current shader clock (the starred level of the
     driver's sysfs table) from a thread while the timed steps run; reports
-    the highest value seen, or None where the table is not readable."""
+    the highest value seen, or None where the table is not readable or the
+    timed region was too short for `min_samples` readings (a short region
+    mostly sees the idle clock, from before the load ramps it up)."""
 
-    def __init__(self, period_s=0.02):
+    def __init__(self, period_s=0.02, min_samples=8):
+        self.min_samples = min_samples
         import glob
         import threading
         paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
@@ -141,7 +144,7 @@ class SclkSampler:
             return None
         self.done.set()
         self.thread.join(timeout=1.0)
-        return max(self.seen) if self.seen else None
+        return max(self.seen) if len(self.seen) >= self.min_samples else None
 
 
 def selector_bytes(lay, keep):
