@@ -56,7 +56,8 @@ class AttnStrategy(ctypes.Structure):
 EXPORTS = ("attn_keep_blocks", "attn_select_workspace_size", "attn_select_blocks",
            "attn_block_sparse_fwd", "attn_dense_fwd", "attn_dense_causal_fwd",
            "attn_strategy_is_sparse", "attn_strategy_workspace_size", "attn_strategy_fwd",
-           "attn_strategy_warmup", "attn_query_support", "attn_last_error", "attn_version")
+           "attn_strategy_warmup", "attn_query_support", "attn_self_test", "attn_last_error",
+           "attn_version")
 
 
 def _load():
@@ -90,6 +91,8 @@ def _load():
     lib.attn_strategy_warmup.restype = I32
     lib.attn_query_support.argtypes = [SH]
     lib.attn_query_support.restype = I32
+    lib.attn_self_test.argtypes = []
+    lib.attn_self_test.restype = I32
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -111,6 +114,14 @@ def last_error() -> str:
 def _check(status: int):
     if status != ATTN_OK:
         raise BsAttnError(status, last_error())
+
+
+def self_test() -> None:
+    """Start-up check on the current device (attn_self_test): a tiny
+    selection and dense, sparse and causal attention run compared with the
+    values their inputs fix. Raises BsAttnError naming the device, the check
+    and the library version on any difference."""
+    _check(lib.attn_self_test())
 
 
 _FIELDS = ("batch", "num_q_heads", "num_kv_heads", "head_dim", "block_q", "block_k", "q_len",
@@ -363,4 +374,4 @@ __all__ = ["BsAttnError", "AttnShape", "AttnStrategy", "EXPORTS", "LIB_PATH", "l
            "last_error", "make_shape", "keep_blocks", "num_blocks", "select_workspace_size",
            "select_blocks", "block_sparse_attention", "dense_attention", "make_strategy",
            "strategy_is_sparse", "strategy_workspace_size", "strategy_forward",
-           "strategy_warmup", "query_support", "pad_segments"]
+           "strategy_warmup", "query_support", "self_test", "pad_segments"]

@@ -43,6 +43,19 @@ attn_status ok() {
   return ATTN_OK;
 }
 
+}  // namespace
+
+namespace bsattn {
+
+attn_status report(attn_status st, const char* fn, const char* msg) {
+  if (st == ATTN_OK) return ok();
+  return fail(st, fn, "%s", msg);
+}
+
+}  // namespace bsattn
+
+namespace {
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Attention workgroups per query block: a workgroup covers at most 128 rows.

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bsattn.h"
+
 namespace bsattn {
 
 // Kernel-side description of one attention call (all sizes validated on the
@@ -64,6 +66,11 @@ hipError_t launch_attention(const AttnParams& p, int head_dim, int block_q, int 
                             hipStream_t stream);
 hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t stream);
 hipError_t launch_score_topk(const ScoreParams& p, int head_dim, int batch, hipStream_t stream);
+
+// Records a failure of entry point `fn` for attn_last_error() (the message
+// gains the library version and target) and returns `st`; ATTN_OK clears
+// the record.
+attn_status report(attn_status st, const char* fn, const char* msg);
 
 // Rows of the score kernel per workgroup and its dynamic LDS bytes.
 int score_rows_per_wg(int n_cand);

@@ -56,7 +56,8 @@ typedef enum attn_status {
   ATTN_ERR_UNSUPPORTED = 2, /* valid, but outside what the kernels implement */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or too small */
   ATTN_ERR_LAUNCH = 4,      /* a kernel launch failed */
-  ATTN_ERR_DEVICE = 5       /* no device, or the current device is not gfx950 */
+  ATTN_ERR_DEVICE = 5,      /* no device, or the current device is not gfx950 */
+  ATTN_ERR_SELF_TEST = 6    /* attn_self_test: a result differs from its known value */
 } attn_status;
 
 typedef struct attn_shape {
@@ -212,6 +213,25 @@ attn_status attn_strategy_warmup(const attn_shape* shape, const attn_strategy* s
  * independently of dense-kernel restrictions). ATTN_OK or the error the
  * entry points would return; attn_last_error() says why. */
 attn_status attn_query_support(const attn_shape* shape);
+
+/* Start-up check (the tiny plan-and-run check at boot of mstar PR #927,
+ * "Since the review"): selects and runs a tiny case on the current device
+ * (2 query heads, 1 KV head, head_dim 128, 64x64 blocks, 100 of 128 query
+ * rows real, a protected prefix of 40 real keys and 88 generation keys, NaN
+ * in every padded row) through attn_select_blocks, attn_block_sparse_fwd,
+ * attn_dense_fwd and attn_dense_causal_fwd, and compares every output with
+ * the value its construction fixes: the keys are scaled one-hot vectors, so
+ * each row's softmax is exactly one-hot on its target key or exactly
+ * uniform over the visible keys; the block list is checked for count, order,
+ * range, the protected block and the -1 fill.
+ * Unlike every other entry point this one allocates (about 0.2 MB of device
+ * memory, freed before it returns), runs on the null stream and synchronises
+ * the device: it is meant for start-up, not for a call path. Returns ATTN_OK;
+ * ATTN_ERR_DEVICE if the device is missing, not a gfx950 or a HIP call fails;
+ * the status of a failing entry point; or ATTN_ERR_SELF_TEST when a result
+ * differs. attn_last_error() then names the device, its architecture, the
+ * check, the position and the values, and the library version. */
+attn_status attn_self_test(void);
 
 /* Description of the last failure on the calling thread ("" if none): the
  * entry point, what failed, the library version and target architecture. */

@@ -203,3 +203,18 @@ def test_strategy_validation_and_workspace():
     assert L.attn_strategy_fwd(_shape(), ctypes.byref(ok), 0, 40, FAKE, FAKE, FAKE, FAKE, None,
                                FAKE, n, None) == 1
     assert "attn_strategy_fwd" in bsa.last_error()
+
+
+def test_self_test_without_a_device_names_the_failure():
+    """With no GPU visible the start-up check reports ATTN_ERR_DEVICE and a
+    message naming itself and the library version; with one it must pass
+    (the GPU suite checks that)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the GPU suite runs the self test")
+    st = bsa.lib.attn_self_test()
+    assert st == 5
+    msg = bsa.last_error()
+    assert "attn_self_test" in msg and bsa.version() in msg and "gfx950" in msg
+    with pytest.raises(bsa.BsAttnError):
+        bsa.self_test()

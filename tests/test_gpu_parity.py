@@ -227,3 +227,13 @@ def test_errors_propagate_from_the_binding():
         bsa.dense_attention(q, k, v, lay)
     with pytest.raises(bsa.BsAttnError, match="keep_blocks"):
         bsa.select_blocks(q, k, case.layout, 0)
+
+
+def test_self_test_passes():
+    """The library's start-up check (tiny select + sparse, dense and causal
+    attention against the values its one-hot inputs fix) passes on this GPU
+    and leaves no error behind."""
+    note("[gpu] attn_self_test")
+    bsa.self_test()
+    assert bsa.last_error() == ""
+    bsa.self_test()  # repeatable: it frees what it allocates
