@@ -53,6 +53,9 @@ WORKLOAD_TEXT = {
                   "512 prefix + 48,360 generation tokens, 64x64 blocks, 75% target (191 of 764)"),
     "mqa48k": ("edge-video-shaped sparse attention, MQA: 32 query heads / 1 KV head, head_dim 128, "
                "512 prefix + 48,360 generation tokens, 64x64 blocks, 75% target (191 of 764)"),
+    "edge48k_cp8": ("one GPU's share of the edge-video-shaped sparse attention split over 8 GPUs "
+                    "by heads: 4 query heads / 1 KV head, head_dim 128, 512 prefix + 48,360 "
+                    "generation tokens (31x30x52), 64x64 blocks, 75% target (191 of 764)"),
     "undcausal": ("understanding-stream causal self-attention: 1,000 tokens padded to 1,024, "
                   "32/8 heads, head_dim 128, 128x128 blocks, bottom-right causal mask"),
 }

@@ -56,6 +56,10 @@ CONFIGS = {
                       frames=(31, 30, 52), bq=64, bk=64, sparsity=75, dist="lowrank"),
     "mqa48k": dict(cfg=8, batch=1, hq=32, hkv=1, d=128, prefix=512, gen=48360,
                    frames=(31, 30, 52), bq=64, bk=64, sparsity=75, dist="lowrank"),
+    # One GPU's share of the 48k workload split over eight GPUs by heads
+    # (4 query heads and their KV head, the full sequence).
+    "edge48k_cp8": dict(cfg=9, batch=1, hq=4, hkv=1, d=128, prefix=512, gen=48360,
+                        frames=(31, 30, 52), bq=64, bk=64, sparsity=75, dist="lowrank"),
     # Two-stream schedule: 36 layers, layers < 8 dense, the rest 75 % sparse.
     "twostream": dict(cfg=5, batch=1, hq=32, hkv=8, d=128, prefix=1000, gen=20000,
                       bq=128, bk=128, sparsity=75, dist="normal",

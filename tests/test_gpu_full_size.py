@@ -87,9 +87,10 @@ def test_edge48k_bench_launch():
 
 
 @pytest.mark.parametrize("name,keep_expected", [
-    ("edge48k_256x128", 96), ("mha64_48k", 191), ("mqa48k", 191)])
+    ("edge48k_256x128", 96), ("mha64_48k", 191), ("mqa48k", 191), ("edge48k_cp8", 191)])
 def test_other_geometries_at_48k(name, keep_expected):
-    """256x128 blocks, MHA at head_dim 64 and MQA at the 48k token shape:
+    """256x128 blocks, MHA at head_dim 64, MQA, and one GPU's share of the
+    head-sharded workload (4 query heads, 1 KV head) at the 48k token shape:
     full selection bit-exact, sampled rows of every head."""
     case = synth.make_config(name)
     lay = case.layout
