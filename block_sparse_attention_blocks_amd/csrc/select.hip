@@ -24,15 +24,19 @@ namespace bsattn {
 namespace {
 
 // ---------------------------------------------------------------- pooling
-// One workgroup per (batch, block, group of 2048 / D heads): thread t owns one
-// 16-byte chunk of one head's row and walks the block's rows. The rows are
-// [rows][heads][D] bf16, so the workgroup's reads stream; eight rows are in
-// flight per thread. Each chunk is summed over the rows in row order, in
-// fp64 (exact for these inputs).
+// One workgroup per (batch, block, group of 2048 / D heads). The group's heads
+// take A = heads x D / 8 threads, one 16-byte chunk of one head's row each;
+// with fewer heads than the group holds, the S = 256 / A thread sets left
+// over split the block's rows among themselves (set s takes rows s, s + S,
+// ...), and set 0 adds the other sets' partial sums through LDS. The rows are
+// [rows][heads][D] bf16, so the reads stream; eight rows are in flight per
+// thread. Sums are fp64 and exact for these inputs, so the split changes no
+// bit of the result.
 template <int D>
 __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
   constexpr int CPH = D / 8;      // 16-byte chunks per head row
   constexpr int HPW = 256 / CPH;  // heads per workgroup
+  __shared__ double part[256 * 8];
   const int blk = blockIdx.x;
   const int b = blockIdx.z;
   const int h0 = blockIdx.y * HPW;
@@ -56,52 +60,66 @@ __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
   const int nblocks = isq ? p.nq : p.nk;
   if (h0 >= heads) return;  // the K blocks need fewer head groups than the Q blocks
 
-  {
-    const int c = (int)threadIdx.x;
-    const bool act = h0 + c / CPH < heads;
-    const int hh = act ? h0 + c / CPH : h0;
-    const int dc = c % CPH;
-    double acc[8];
+  const int A = min(HPW, heads - h0) * CPH;  // threads per row set
+  const int S = 256 / A;                     // row sets
+  const int c = (int)threadIdx.x;
+  const int set = c / A, cc = c % A;
+  const bool act = set < S;
+  const int hh = h0 + cc / CPH;
+  const int dc = cc % CPH;
+  double acc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
-    if (act && n > 0) {
-      const uint16_t* src = base + (int64_t)start * s1 + (int64_t)hh * s2 + dc * 8;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  if (act) {
+    const uint16_t* src = base + (int64_t)start * s1 + (int64_t)hh * s2 + dc * 8;
 #pragma unroll 8
-      for (int t = 0; t < n; ++t) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)t * s1);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int t = set; t < n; t += S) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)t * s1);
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += (double)__uint_as_float(w[e] << 16);
-          acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
-        }
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+        acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
       }
     }
-    float m32[8];
-    double sq = 0.0;
-    const double dn = (double)max(n, 1);
+  }
+  if (S > 1) {  // uniform over the workgroup
+    if (act && set > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      m32[e] = n > 0 ? (float)(acc[e] / dn) : 0.0f;  // one fp64 division, one fp32 rounding
-      sq = __builtin_fma((double)m32[e], (double)m32[e], sq);
+      for (int e = 0; e < 8; ++e) part[e * 256 + c] = acc[e];
     }
+    __syncthreads();
+    if (set == 0) {
+      for (int s = 1; s < S; ++s)
 #pragma unroll
-    for (int off = 1; off < CPH; off <<= 1) sq += __shfl_xor(sq, off);
-    if (act) {
-      if (isq) {
-        double* dst = p.qp + (((int64_t)b * p.hq + hh) * p.nq + j) * D + dc * 8;
+        for (int e = 0; e < 8; ++e) acc[e] += part[e * 256 + s * A + cc];
+    }
+  }
+  float m32[8];
+  double sq = 0.0;
+  const double dn = (double)max(n, 1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[e] = (double)m32[e];
-      } else {
-        float* dst = p.kpt + (((int64_t)b * p.hkv + hh) * D + dc * 8) * p.nk + j;
+  for (int e = 0; e < 8; ++e) {
+    m32[e] = n > 0 ? (float)(acc[e] / dn) : 0.0f;  // one fp64 division, one fp32 rounding
+    sq = __builtin_fma((double)m32[e], (double)m32[e], sq);
+  }
+  // The CPH threads of one head row are consecutive lanes of one wave.
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[(int64_t)e * p.nk] = m32[e];
-      }
-      if (dc == 0) {
-        // Upper bound of the Euclidean norm (covers the rounding of sq and sqrt).
-        const double nrm = __builtin_sqrt(sq) * (1.0 + 0x1p-40);
-        (isq ? p.qn : p.kn)[((int64_t)b * heads + hh) * nblocks + j] = nrm;
-      }
+  for (int off = 1; off < CPH; off <<= 1) sq += __shfl_xor(sq, off);
+  if (set == 0) {
+    if (isq) {
+      double* dst = p.qp + (((int64_t)b * p.hq + hh) * p.nq + j) * D + dc * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[e] = (double)m32[e];
+    } else {
+      float* dst = p.kpt + (((int64_t)b * p.hkv + hh) * D + dc * 8) * p.nk + j;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[(int64_t)e * p.nk] = m32[e];
+    }
+    if (dc == 0) {
+      // Upper bound of the Euclidean norm (covers the rounding of sq and sqrt).
+      const double nrm = __builtin_sqrt(sq) * (1.0 + 0x1p-40);
+      (isq ? p.qn : p.kn)[((int64_t)b * heads + hh) * nblocks + j] = nrm;
     }
   }
 }
@@ -247,9 +265,13 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Every product of two fp32 values is exact in fp64 and each accumulation is
 // rounded once, so the rigorous error bound of an fp64 dot product applies.
 // Phase 2: each wave takes rows and selects the top blocks by bisection on
-// the 32-bit keys, then writes the list in ascending block order.
+// the 32-bit keys, then writes the list in ascending block order. Eight
+// waves share both phases, which halves a workgroup's latency against four
+// (what decides the time when few heads give fewer workgroups than CUs).
+constexpr int kScoreWaves = 8;
+
 template <int D, int R>
-__global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
+__global__ void __launch_bounds__(64 * kScoreWaves) score_topk_kernel(const ScoreParams p) {
   extern __shared__ uint32_t keys_lds[];
   typedef double f64x4 __attribute__((ext_vector_type(4)));
   constexpr int KST = D / 4;  // MFMA k-steps over D
@@ -275,7 +297,7 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
     for (int st = 0; st < KST; ++st) qa[st] = qr[4 * st];
   }
   const int ntiles = (ncand + 15) >> 4;
-  for (int tile = wave; tile < ntiles; tile += 4) {
+  for (int tile = wave; tile < ntiles; tile += kScoreWaves) {
     const int c = tile * 16 + arow;  // candidate of this lane (B column, result column)
     const int j = p.n_prefix_blocks + min(c, ncand - 1);
     const float* kc = kcols + j + (int64_t)kq * p.nk;
@@ -308,7 +330,7 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
   // Exact recomputation of the marked scores (rare: a few in a hundred
   // thousand for typical inputs, but any number is handled), one whole wave
   // per score.
-  for (int e0 = wave * 64; e0 < nrows * ncp; e0 += 256) {
+  for (int e0 = wave * 64; e0 < nrows * ncp; e0 += 64 * kScoreWaves) {
     const int e = e0 + lane;
     uint64_t marked = __builtin_amdgcn_ballot_w64(e < nrows * ncp && keys_lds[e] == kUndecided);
     while (marked != 0) {
@@ -326,7 +348,7 @@ __global__ void __launch_bounds__(256) score_topk_kernel(const ScoreParams p) {
   const bool take_all = rsel == ncand;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int M = ncp >> 6;
-  for (int r = wave; r < nrows; r += 4) {
+  for (int r = wave; r < nrows; r += kScoreWaves) {
     const int i = i0 + r;
     const int64_t row_id = ((int64_t)b * p.hq + h) * p.nq + i;
     int32_t* out = p.idx + row_id * p.idx_row_stride;
@@ -467,14 +489,14 @@ hipError_t launch_score_topk(const ScoreParams& p, int head_dim, int batch, hipS
   if (attr_status != hipSuccess) return attr_status;
   if (head_dim == 128) {
     if (rows == 16)
-      hipLaunchKernelGGL((score_topk_kernel<128, 16>), grid, dim3(256), lds, stream, p);
+      hipLaunchKernelGGL((score_topk_kernel<128, 16>), grid, dim3(64 * kScoreWaves), lds, stream, p);
     else
-      hipLaunchKernelGGL((score_topk_kernel<128, 8>), grid, dim3(256), lds, stream, p);
+      hipLaunchKernelGGL((score_topk_kernel<128, 8>), grid, dim3(64 * kScoreWaves), lds, stream, p);
   } else {
     if (rows == 16)
-      hipLaunchKernelGGL((score_topk_kernel<64, 16>), grid, dim3(256), lds, stream, p);
+      hipLaunchKernelGGL((score_topk_kernel<64, 16>), grid, dim3(64 * kScoreWaves), lds, stream, p);
     else
-      hipLaunchKernelGGL((score_topk_kernel<64, 8>), grid, dim3(256), lds, stream, p);
+      hipLaunchKernelGGL((score_topk_kernel<64, 8>), grid, dim3(64 * kScoreWaves), lds, stream, p);
   }
   return hipGetLastError();
 }
