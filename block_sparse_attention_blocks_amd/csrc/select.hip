@@ -24,19 +24,20 @@ namespace bsattn {
 namespace {
 
 // ---------------------------------------------------------------- pooling
-// One workgroup per (batch, block, group of 2048 / D heads). The group's heads
-// take A = heads x D / 8 threads, one 16-byte chunk of one head's row each;
-// with fewer heads than the group holds, the S = 256 / A thread sets left
-// over split the block's rows among themselves (set s takes rows s, s + S,
-// ...), and set 0 adds the other sets' partial sums through LDS. The rows are
-// [rows][heads][D] bf16, so the reads stream; eight rows are in flight per
-// thread. Sums are fp64 and exact for these inputs, so the split changes no
-// bit of the result.
+// One workgroup of 512 threads per (batch, block, group of 2048 / D heads).
+// The group's heads take A = heads x D / 8 threads, one 16-byte chunk of one
+// head's row each; the S = min(512 / A, 8) thread sets split the block's
+// rows among themselves (set s takes rows s, s + S, ...), and set 0 adds the
+// other sets' partial sums through LDS. The rows are [rows][heads][D] bf16,
+// so the reads stream; eight rows are in flight per thread. Sums are fp64
+// and exact for these inputs, so the split changes no bit of the result.
+constexpr int kPoolThreads = 512;
+
 template <int D>
-__global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
+__global__ void __launch_bounds__(kPoolThreads) pool_kernel(const PoolParams p) {
   constexpr int CPH = D / 8;      // 16-byte chunks per head row
   constexpr int HPW = 256 / CPH;  // heads per workgroup
-  __shared__ double part[256 * 8];
+  __shared__ double part[kPoolThreads * 8];
   const int blk = blockIdx.x;
   const int b = blockIdx.z;
   const int h0 = blockIdx.y * HPW;
@@ -61,7 +62,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
   if (h0 >= heads) return;  // the K blocks need fewer head groups than the Q blocks
 
   const int A = min(HPW, heads - h0) * CPH;  // threads per row set
-  const int S = 256 / A;                     // row sets
+  const int S = min(kPoolThreads / A, 8);    // row sets (set 0 adds the others one by one)
   const int c = (int)threadIdx.x;
   const int set = c / A, cc = c % A;
   const bool act = set < S;
@@ -86,13 +87,13 @@ __global__ void __launch_bounds__(256) pool_kernel(const PoolParams p) {
   if (S > 1) {  // uniform over the workgroup
     if (act && set > 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[e * 256 + c] = acc[e];
+      for (int e = 0; e < 8; ++e) part[e * kPoolThreads + c] = acc[e];
     }
     __syncthreads();
     if (set == 0) {
       for (int s = 1; s < S; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += part[e * 256 + s * A + cc];
+        for (int e = 0; e < 8; ++e) acc[e] += part[e * kPoolThreads + s * A + cc];
     }
   }
   float m32[8];
@@ -462,9 +463,9 @@ hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t
   const dim3 grid(p.nq + p.nk, (hmax + hpw - 1) / hpw, batch);
   if (grid.x == 0) return hipSuccess;
   if (head_dim == 128)
-    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(kPoolThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(kPoolThreads), 0, stream, p);
   return hipGetLastError();
 }
 
