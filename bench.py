@@ -106,6 +106,29 @@ def recorded_traffic(name):
         return None
 
 
+def recorded_mfma_busy(name):
+    """Share of the attention dispatch's cycles in which the matrix cores were
+    busy (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs),
+    from the committed counter summary, if it covers this workload and was
+    taken on the current kernel source; else None. Unlike the fraction of
+    the published peak it does not depend on the shader clock."""
+    path = os.path.join(PROFILES, "attn_fwd_mfma_busy_edge48k_dense8k.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#") and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals[f"{name}_mfma_busy_frac"])
+    except (KeyError, ValueError):
+        return None
+
+
 class SclkSampler:
     """Samples the GPU's current shader clock (the starred level of the
     driver's sysfs table) from a thread while the timed steps run; reports
@@ -474,6 +497,7 @@ def main():
         # the bf16 MFMA peak scales with the shader clock (4096 FLOP per CU per cycle)
         "attn_frac_of_peak_at_seen_clock": (round(att_tflops / (256 * 4096 * sclk * 1e6 / 1e12), 4)
                                             if sclk else None),
+        "attn_mfma_busy_frac_counters": recorded_mfma_busy(name),
         "effective_tflop_per_step": round(eff_flops / 1e12, 4),
         "roofline": {
             "kernel": kname,
