@@ -164,16 +164,59 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
-def _check_tensor(t, name, dtype, device=None):
+def _check_kind(t, name, dtype, shape=None, seq_dim=None):
+    """Type, dtype and shape; with ``seq_dim``, that dimension may hold more
+    entries than the layout uses (rows past the layout are never touched)."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is None:
+        return
+    got = tuple(t.shape)
+    ok = len(got) == len(shape) and all(
+        g >= w if i == seq_dim else g == w for i, (g, w) in enumerate(zip(got, shape)))
+    if not ok:
+        need = "at least " if seq_dim is not None else ""
+        raise ValueError(f"{name} has shape {got}, the layout needs {tuple(shape)}"
+                         + (f" ({need}{shape[seq_dim]} along dim {seq_dim})" if seq_dim is not None else ""))
+
+
+def _check_device(t, name, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_operands(layout, q, k=None, v=None, out=None, block_idx=None, block_cnt=None):
+    """dtype, exact shape and device of every tensor a call reads or writes:
+    the library sees only pointers and strides, so a tensor smaller than the
+    layout says would be read or written out of bounds. Shapes are checked
+    before devices."""
+    import torch
+    b, d = int(layout["batch"]), int(layout["head_dim"])
+    hq, hkv = int(layout["num_q_heads"]), int(layout["num_kv_heads"])
+    lq, lk = int(layout["q_len"]), int(layout["kv_len"])
+    nq, _, _ = num_blocks(layout)
+    # [B, L, H, D] tensors may hold more rows than the layout's length
+    named = [(q, "q", torch.bfloat16, (b, lq, hq, d), 1), (k, "k", torch.bfloat16, (b, lk, hkv, d), 1),
+             (v, "v", torch.bfloat16, (b, lk, hkv, d), 1),
+             (out, "out", torch.bfloat16, (b, lq, hq, d), 1)]
+    if block_idx is not None:
+        if not isinstance(block_idx, torch.Tensor) or block_idx.dim() != 4 or block_idx.shape[-1] < 1:
+            raise ValueError("block_idx must be an int32 tensor [B, Hq, NQ, row] with row >= 1")
+        named.append((block_idx, "block_idx", torch.int32, (b, hq, nq, int(block_idx.shape[-1])), None))
+    named.append((block_cnt, "block_cnt", torch.int32, (b, hq, nq), None))
+    present = [x for x in named if x[0] is not None]
+    for t, n, dt, shp, sd in present:
+        _check_kind(t, n, dt, shp, sd)
+    for t, n, _, _, _ in present:
+        _check_device(t, n, q.device)
+    for t, n in ((block_idx, "block_idx"), (block_cnt, "block_cnt")):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
 
 
 def keep_blocks(n_kv_blocks: int, n_protected: int, sparsity_pct: int) -> int:
@@ -203,13 +246,15 @@ def select_blocks(q, k, layout, keep: int, idx_row_stride=None, *, block_idx=Non
     """Per-query-head KV-block indices and counts (attn_select_blocks).
     Returns (block_idx [B,Hq,NQ,stride] int32, block_cnt [B,Hq,NQ] int32)."""
     import torch
-    _check_tensor(q, "q", torch.bfloat16)
-    _check_tensor(k, "k", torch.bfloat16, q.device)
+    _check_operands(layout, q, k, block_idx=block_idx, block_cnt=block_cnt)
     shape = make_shape(layout, q=q, k=k)
     nq, nk, _ = num_blocks(layout)
     stride = int(keep if idx_row_stride is None else idx_row_stride)
     stride = max(stride, 1)
     b, hq = int(layout["batch"]), int(layout["num_q_heads"])
+    if block_idx is not None and int(block_idx.shape[-1]) != stride:
+        raise ValueError(f"block_idx rows hold {int(block_idx.shape[-1])} entries, "
+                         f"idx_row_stride is {stride}")
     if block_idx is None:
         block_idx = torch.empty((b, hq, nq, stride), dtype=torch.int32, device=q.device)
     if block_cnt is None:
@@ -228,13 +273,9 @@ def block_sparse_attention(q, k, v, block_idx, block_cnt, layout, *, out=None, r
                            stream=None):
     """Attention over the selected blocks (attn_block_sparse_fwd)."""
     import torch
-    _check_tensor(q, "q", torch.bfloat16)
-    for t, n in ((k, "k"), (v, "v")):
-        _check_tensor(t, n, torch.bfloat16, q.device)
-    _check_tensor(block_idx, "block_idx", torch.int32, q.device)
-    _check_tensor(block_cnt, "block_cnt", torch.int32, q.device)
-    if not (block_idx.is_contiguous() and block_cnt.is_contiguous()):
-        raise ValueError("block_idx and block_cnt must be contiguous")
+    if block_idx is None or block_cnt is None:
+        raise ValueError("block_idx and block_cnt are required")
+    _check_operands(layout, q, k, v, out, block_idx, block_cnt)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = None
@@ -253,9 +294,7 @@ def dense_attention(q, k, v, layout, *, causal=False, out=None, return_lse=False
     ``causal``, causal dense attention bottom-right aligned over the real
     tokens (attn_dense_causal_fwd)."""
     import torch
-    _check_tensor(q, "q", torch.bfloat16)
-    for t, n in ((k, "k"), (v, "v")):
-        _check_tensor(t, n, torch.bfloat16, q.device)
+    _check_operands(layout, q, k, v, out)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = None
@@ -307,9 +346,7 @@ def strategy_forward(q, k, v, layout, strategy: AttnStrategy, step: int, layer: 
     """The attention of (step, layer) under ``strategy`` (attn_strategy_fwd):
     dense, or selection + block-sparse attention."""
     import torch
-    _check_tensor(q, "q", torch.bfloat16)
-    for t, n in ((k, "k"), (v, "v")):
-        _check_tensor(t, n, torch.bfloat16, q.device)
+    _check_operands(layout, q, k, v, out)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     lse = None
@@ -328,6 +365,7 @@ def strategy_warmup(q, k, v, layout, strategy: AttnStrategy, *, out=None, worksp
                     stream=None):
     """Run every kind of call the strategy makes once (attn_strategy_warmup)."""
     import torch
+    _check_operands(layout, q, k, v, out)
     if out is None:
         out = torch.empty_like(q, memory_format=torch.contiguous_format)
     ws, nbytes = _strategy_ws(layout, strategy, workspace, q.device)

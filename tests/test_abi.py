@@ -218,3 +218,32 @@ def test_self_test_without_a_device_names_the_failure():
     assert "attn_self_test" in msg and bsa.version() in msg and "gfx950" in msg
     with pytest.raises(bsa.BsAttnError):
         bsa.self_test()
+
+
+def test_binding_checks_tensor_shapes_against_the_layout():
+    """The library sees only pointers and strides, so the binding refuses a
+    tensor whose shape differs from what the layout implies (before touching
+    the device)."""
+    import synth
+    lay = synth.make_case("shape_chk", hq=2, hkv=1, d=64, prefix=64, gen=448, cfg=1).layout
+    b, lq, lk = lay["batch"], lay["q_len"], lay["kv_len"]
+    q = torch.zeros((b, lq, 2, 64), dtype=torch.bfloat16)
+    k = torch.zeros((b, lk, 1, 64), dtype=torch.bfloat16)
+    short_q = torch.zeros((b, lq - 64, 2, 64), dtype=torch.bfloat16)
+    long_q = torch.zeros((b, lq + 64, 2, 64), dtype=torch.bfloat16)  # extra rows are allowed
+    wide_k = torch.zeros((b, lk, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="shape"):
+        bsa.select_blocks(short_q, k, lay, 4)
+    with pytest.raises(ValueError, match="shape"):
+        bsa.select_blocks(q, wide_k, lay, 4)
+    with pytest.raises(ValueError, match="shape"):
+        bsa.dense_attention(q, k, k, lay, out=short_q)
+    nq = lq // lay["block_q"]
+    idx = torch.zeros((b, 2, nq - 1, 4), dtype=torch.int32)
+    cnt = torch.zeros((b, 2, nq), dtype=torch.int32)
+    with pytest.raises(ValueError, match="shape"):
+        bsa.block_sparse_attention(q, k, k, idx, cnt, lay)
+    with pytest.raises(ValueError, match="GPU"):  # right shapes, wrong device
+        bsa.dense_attention(q, k, k, lay)
+    with pytest.raises(ValueError, match="GPU"):
+        bsa.dense_attention(long_q, k, k, lay)

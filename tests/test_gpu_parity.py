@@ -222,8 +222,12 @@ def test_selector_at_its_block_limit(bk, d):
 def test_errors_propagate_from_the_binding():
     case = synth.make_config("tiny")
     q, k, v = case_to_gpu(case)
-    lay = dict(case.layout, num_kv_heads=3)
+    lay = dict(case.layout, num_kv_heads=3)  # 2 query heads: not a multiple of 3
+    k3 = torch.zeros((k.shape[0], k.shape[1], 3, k.shape[3]), dtype=k.dtype, device=k.device)
     with pytest.raises(bsa.BsAttnError, match="INVALID_ARG"):
+        bsa.dense_attention(q, k3, k3, lay)
+    # tensors that do not match the layout never reach the library
+    with pytest.raises(ValueError, match="shape"):
         bsa.dense_attention(q, k, v, lay)
     with pytest.raises(bsa.BsAttnError, match="keep_blocks"):
         bsa.select_blocks(q, k, case.layout, 0)
@@ -237,3 +241,54 @@ def test_self_test_passes():
     bsa.self_test()
     assert bsa.last_error() == ""
     bsa.self_test()  # repeatable: it frees what it allocates
+
+
+@pytest.mark.parametrize("d,bq,bk", [(128, 64, 64), (64, 128, 128)])
+def test_strided_views_match_contiguous(d, bq, bk):
+    """Q, K, V and the output as strided views (Q and O inside wider per-token
+    rows, K head-major, V with padded rows), with NaN everywhere outside the
+    views: selection, sparse, dense and causal results are bitwise those of
+    contiguous tensors (the strides only move the addresses)."""
+    case = synth.make_case(f"strided{d}", hq=4, hkv=2, d=d, bq=bq, bk=bk, prefix=100, gen=700,
+                           cfg=54 + d)
+    lay = case.layout
+    b, lq, lk = lay["batch"], lay["q_len"], lay["kv_len"]
+    hq, hkv = lay["num_q_heads"], lay["num_kv_heads"]
+    note(f"[gpu] strided views {lay}")
+    q, k, v = case_to_gpu(case)
+    nan = float("nan")
+    qbuf = torch.full((b, lq, hq + 3, d), nan, dtype=torch.bfloat16, device=q.device)
+    qs = qbuf[:, :, 1:1 + hq]
+    qs.copy_(q)
+    kbuf = torch.full((b, hkv, lk, d), nan, dtype=torch.bfloat16, device=q.device)
+    ks = kbuf.permute(0, 2, 1, 3)
+    ks.copy_(k)
+    vbuf = torch.full((b, lk, hkv, d + 64), nan, dtype=torch.bfloat16, device=q.device)
+    vs = vbuf[..., :d]
+    vs.copy_(v)
+    obuf = torch.full((b, lq, hq + 2, d), nan, dtype=torch.bfloat16, device=q.device)
+    os_ = obuf[:, :, 2:]
+    assert not (qs.is_contiguous() or ks.is_contiguous() or vs.is_contiguous()
+                or os_.is_contiguous())
+    keep = _keep(lay, 60)
+    idx, cnt = bsa.select_blocks(q, k, lay, keep)
+    idx_s, cnt_s = bsa.select_blocks(qs, ks, lay, keep)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s) and torch.equal(cnt, cnt_s)
+    runs = [
+        (lambda o: bsa.block_sparse_attention(q, k, v, idx, cnt, lay, out=o),
+         lambda o: bsa.block_sparse_attention(qs, ks, vs, idx, cnt, lay, out=o)),
+        (lambda o: bsa.dense_attention(q, k, v, lay, out=o),
+         lambda o: bsa.dense_attention(qs, ks, vs, lay, out=o)),
+        (lambda o: bsa.dense_attention(q, k, v, lay, causal=True, out=o),
+         lambda o: bsa.dense_attention(qs, ks, vs, lay, causal=True, out=o)),
+    ]
+    for contiguous, strided in runs:
+        ref = torch.empty_like(q)
+        contiguous(ref)
+        obuf.fill_(nan)
+        strided(os_)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int16), os_.contiguous().view(torch.int16))
+        # nothing outside the output view was written
+        assert torch.isnan(obuf[:, :, :2].float()).all()
