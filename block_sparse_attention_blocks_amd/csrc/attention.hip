@@ -17,12 +17,13 @@
 // halves; wave (qh, kh) computes query rows [32 qh, 32 qh + 32) against keys
 // [32 kh, 32 kh + 32) of every stage, so every K/V stage in LDS feeds all the
 // block's rows. Each wave keeps its own partial softmax state; the two key
-// halves are merged once at the end. A wave needs fewer than 256 registers,
-// so every SIMD runs two waves (two 4-wave workgroups per CU at 64-row
-// blocks, one 8-wave workgroup at 128-row blocks; a 256-row block runs as two
-// 128-row workgroups on the same list): while one wave waits (LDS,
-// barrier, the HBM copies) the other issues, and one wave's softmax overlaps
-// the other's matrix products.
+// halves are merged once at the end. At head_dim 128 a wave needs fewer than
+// 256 registers, so every SIMD runs two waves (two 4-wave workgroups per CU
+// at 64-row blocks, one 8-wave workgroup at 128-row blocks; a 256-row block
+// runs as two 128-row workgroups on the same list); at head_dim 64 it needs
+// fewer than 168 and a SIMD runs three (three 64-row workgroups per CU).
+// While one wave waits (LDS, barrier, the HBM copies) another issues, and one
+// wave's softmax overlaps another's matrix products.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K fragment (A operand)
 //    comes from LDS, Q^T (B operand) stays in registers for the whole
 //    kernel. Each lane owns one query row and half of the 32 keys, so the
@@ -273,9 +274,12 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   // XCD whose second 32 start about half a workgroup lifetime after the
   // first 32 (measured). Starting those at the middle of their lists keeps
   // all the XCD's workgroups at about the same place in the KV sequence at
-  // any time, so they share the blocks in L2. The order depends on blockIdx
-  // only, so results stay bitwise reproducible.
-  const int n_first = (NQG == 2 && ((w >> 3) & 32)) ? nblk / 2 : 0;
+  // any time, so they share the blocks in L2. At head_dim 64 a CU holds
+  // three 64-row workgroups, and the three cohorts of 32 start a third of
+  // their lists apart. The order depends on blockIdx only, so results stay
+  // bitwise reproducible.
+  const int cohort = (w >> 8) % (D == 64 ? 3 : 2);  // (w / 8) / 32: cohorts of 32 per XCD
+  const int n_first = (NQG == 2) ? (cohort * nblk) / (D == 64 ? 3 : 2) : 0;
 
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
@@ -628,8 +632,14 @@ constexpr int smem_elems() {
   return stages > handover ? stages : handover;
 }
 
+// Waves per SIMD: two at head_dim 128 (up to 256 VGPRs each), three at
+// head_dim 64 (up to 168; the kernel needs about 160 there).
+template <int D>
+constexpr int waves_per_simd() { return D == 64 ? 3 : 2; }
+
 template <int D, int BK, int NQG, int MODE>
-__global__ void __launch_bounds__(128 * NQG) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ void __launch_bounds__(128 * NQG)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<D>(), waves_per_simd<D>())))
 attn_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[smem_elems<D, NQG>()];
   attn_fwd_body<D, BK, NQG, MODE>(p, smem);
