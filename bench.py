@@ -300,8 +300,8 @@ def cpu_baseline(case, keep, n_blocks, n_heads):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the kernel on one GPU's share); "
-              "--gpus above 1 is not supported", file=sys.stderr)
+        print("bench.py: runs on one GPU only; --gpus above 1 is not supported (one GPU's share "
+              "of the head-sharded 48k workload is --workload edge48k_cp8)", file=sys.stderr)
         sys.exit(2)
 
     import torch
