@@ -280,6 +280,21 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   // bitwise reproducible.
   const int cohort = (w >> 8) % (D == 64 ? 3 : 2);  // (w / 8) / 32: cohorts of 32 per XCD
   const int n_first = (NQG == 2) ? (cohort * nblk) / (D == 64 ? 3 : 2) : 0;
+  // The list, 64 positions at a time: lane l of lw_cur holds list position
+  // 64 lw_c + l (after the rotation), lw_next the next 64. Each chunk is one
+  // vector load issued a whole chunk before its first use, so reading the
+  // list never waits on memory.
+  int lw_cur = -1, lw_next = -1, lw_c = 0;
+  auto load_chunk = [&](int c) -> int {
+    const int pos = c * 64 + lane;
+    int n = pos + n_first;
+    if (n >= nblk) n -= nblk;
+    return pos < nblk ? idx_row[n] : -1;
+  };
+  if constexpr (!DENSE) {
+    lw_cur = load_chunk(0);
+    lw_next = load_chunk(1);
+  }
 
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
@@ -301,7 +316,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     if constexpr (DENSE) {
       return n < p.n_forced ? n : p.n_prefix_blocks + (n - p.n_forced);
     } else {
-      return scalar_load_i32(idx_row + n);
+      return __builtin_amdgcn_readlane(lw_cur, n_pos & 63);  // n_pos lies in chunk lw_c
     }
   };
   // Real keys of block j form a prefix [0, nvalid) of the block: segments
@@ -437,6 +452,13 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     const bool last_sub = (u % SPB) == SPB - 1;
     const int n = u / SPB;
     if (last_sub) {
+      if constexpr (!DENSE) {
+        if (n + 2 < nblk && ((n + 2) & 63) == 0) {
+          lw_cur = lw_next;
+          ++lw_c;
+          lw_next = load_chunk(lw_c + 1);
+        }
+      }
       j2 = (n + 2 < nblk) ? block_of(n + 2) : -1;
       nv2 = (n + 2 < nblk) ? nvalid_of(j2) : 0;
     }
