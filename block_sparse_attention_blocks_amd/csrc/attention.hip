@@ -233,17 +233,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int row0 = (i * p.qparts + part) * (32 * NQG);
   const int qrow = row0 + 32 * qh + col;
 
-  // Q^T fragments (B operand): the lane holds q[qrow][16 ks + 8 half .. +7].
-  bf16x8 qf[KS];
-  {
-    const uint16_t* qp =
-        p.q + (int64_t)b * p.qs0 + (int64_t)qrow * p.qs1 + (int64_t)h * p.qs2 + half * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
-    // Retire these loads now: the stage copies are counted on the same
-    // vector-memory counter and are awaited explicitly.
-    wait_vmcnt<0>();
-  }
 
   int nblk;
   const int32_t* idx_row = nullptr;
@@ -294,6 +283,16 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   if constexpr (!DENSE) {
     lw_cur = load_chunk(0);
     lw_next = load_chunk(1);
+  }
+  // Q^T fragments (B operand): the lane holds q[qrow][16 ks + 8 half .. +7].
+  // Issued after the list's first chunks (whose first use waits only for
+  // those) and awaited together with the first stage copies.
+  bf16x8 qf[KS];
+  {
+    const uint16_t* qp =
+        p.q + (int64_t)b * p.qs0 + (int64_t)qrow * p.qs1 + (int64_t)h * p.qs2 + half * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
 
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
