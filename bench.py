@@ -3,11 +3,14 @@ edge-video-shaped workload, one MI355X.
 
 One step = the whole hot path over synthetic inputs already in HBM: block
 selection (pooling + scores + top-k) followed by block-sparse attention
-(``edge48k``, ``video720p``); dense attention alone (``dense8k``); causal
-dense attention of the understanding stream over itself (``undcausal``); or
-the 36-layer two-stream schedule (``twostream``): per layer the understanding
-stream's causal self-attention, then the generation stream over cat(und, gen),
-dense for the first 8 layers and selected-sparse for the other 28. Prints one JSON line. ``value`` is effective attention
+(``edge48k``, ``video720p``, and at the 48k token shape ``edge48k_256x128``
+with 256x128 blocks, ``mha64_48k``, ``mqa48k`` and ``edge48k_cp8``, one GPU's
+4-head share of the head-sharded workload); dense attention alone
+(``dense8k``); causal dense attention of the understanding stream over itself
+(``undcausal``); or the 36-layer two-stream schedule (``twostream``): per
+layer the understanding stream's causal self-attention, then the generation
+stream over cat(und, gen), dense for the first 8 layers and selected-sparse
+for the other 28. Prints one JSON line. ``value`` is effective attention
 TFLOP/s of the step (4 * block_q * block_k * head_dim FLOP per selected tile,
 selection time included in the denominator); the attention kernel alone is
 reported in ``roofline`` against the bf16 MFMA peak, timed with HIP events on
