@@ -493,10 +493,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
 
-    // A wave in phase (a), whose exponentials feed the next PV products and
-    // whose copies feed the next stages, gets issue priority over a wave in
-    // phase (b) on the same SIMD (0.3-1.7 % at 48k, about 1 % dense).
-    __builtin_amdgcn_s_setprio(1);
     // ---- (a) S[u+1] = K Q^T || exponentials of P[u] || V^T reads || copies.
     bf16x8 pf[2];
     bf16x4 vf[2][DT][2];
@@ -550,7 +546,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     const int nvs_next = (u + 1 < nst) ? nvs_of((SPB == 1 || last_sub) ? nv1 : nv0, u + 1) : 0;
     mask(s_nxt, nvs_next,
          CAUSAL ? rank0_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) : 0);
-    __builtin_amdgcn_s_setprio(0);
     // ---- (b) O += V^T P[u]^T || row max of S[u+1].
     float mxl = -__builtin_inff();
     constexpr int NPV = 2 * DT;
