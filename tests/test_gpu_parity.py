@@ -292,3 +292,34 @@ def test_strided_views_match_contiguous(d, bq, bk):
         assert torch.equal(ref.view(torch.int16), os_.contiguous().view(torch.int16))
         # nothing outside the output view was written
         assert torch.isnan(obuf[:, :, :2].float()).all()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_list_chunk_boundaries(d):
+    """Block lists of 64, 65, 129 and 140 entries (the kernel reads a list 64
+    entries per vector load, and some workgroups start in the middle of their
+    list): with every block listed the result is bitwise the dense one, and
+    shorter lists match the oracle on sampled rows. 140 query blocks x 4
+    heads = 560 workgroups, so every rotation cohort occurs."""
+    case = synth.make_case(f"chunks{d}", hq=4, hkv=1, d=d, prefix=0, gen=64 * 140 - 20, cfg=60 + d)
+    lay = case.layout
+    q, k, v = case_to_gpu(case)
+    nq, nk, p = bsa.num_blocks(lay)
+    assert nk == 140 and nq * 4 > 512
+    note(f"[gpu] list chunk boundaries d={d} {lay}")
+    idx, cnt = bsa.select_blocks(q, k, lay, nk)
+    a = bsa.block_sparse_attention(q, k, v, idx, cnt, lay)
+    b = bsa.dense_attention(q, k, v, lay)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    rows = synth.sample_rows(case, 48)
+    for keep in (64, 65, 129):
+        idx, cnt = bsa.select_blocks(q, k, lay, keep)
+        out, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, return_lse=True)
+        torch.cuda.synchronize()
+        ridx, rcnt = oracle.select(lay, case.q, case.k, keep)
+        assert np.array_equal(idx.cpu().numpy(), ridx) and np.array_equal(cnt.cpu().numpy(), rcnt)
+        ro, _ = oracle.attend_rows(lay, case.q, case.k, case.v, ridx, rcnt, rows)
+        g = out_to_f64(out)
+        got = np.stack([g[0, rows[0, h], h] for h in range(4)])[None]
+        assert_close(got, ro, what=f"keep {keep}")
