@@ -323,3 +323,19 @@ def test_list_chunk_boundaries(d):
         g = out_to_f64(out)
         got = np.stack([g[0, rows[0, h], h] for h in range(4)])[None]
         assert_close(got, ro, what=f"keep {keep}")
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_large_and_growing_logits(d):
+    """Logits of a few hundred that grow along the key sequence (Q scaled by
+    8, keys by a ramp from 1/4 to 4): the running maximum moves often and by
+    large steps, so the lazy rescaling and the underflow of small weights
+    are exercised; outputs, lse and the selection still match the oracle."""
+    import dataclasses
+    base = synth.make_case(f"biglogits{d}", hq=4, hkv=2, d=d, prefix=100, gen=700, cfg=80 + d)
+    lay = base.layout
+    qf = synth.bf16_bits_to_f32(base.q).astype(np.float64) * 8.0
+    ramp = np.geomspace(0.25, 4.0, lay["kv_len"])[None, :, None, None]
+    kf = synth.bf16_bits_to_f32(base.k).astype(np.float64) * ramp
+    case = dataclasses.replace(base, q=synth.to_bf16_bits(qf), k=synth.to_bf16_bits(kf))
+    _full_check(case, 60)
