@@ -234,7 +234,9 @@ attn_status attn_query_support(const attn_shape* shape);
 attn_status attn_self_test(void);
 
 /* Description of the last failure on the calling thread ("" if none): the
- * entry point, what failed, the library version and target architecture. */
+ * entry point, what failed, the library version and target architecture.
+ * The string belongs to the library and stays valid until the next call of
+ * an entry point on the same thread. */
 const char* attn_last_error(void);
 
 /* Library version string. */

@@ -247,3 +247,44 @@ def test_binding_checks_tensor_shapes_against_the_layout():
         bsa.dense_attention(q, k, k, lay)
     with pytest.raises(ValueError, match="GPU"):
         bsa.dense_attention(long_q, k, k, lay)
+
+
+def test_header_is_plain_c_and_a_c_program_links(tmp_path):
+    """The boundary is a C ABI: the header compiles as C99 with gcc (no HIP or
+    torch headers), and a C program linked against libbsattn.so calls the
+    host-only entry points and gets the documented answers."""
+    src = tmp_path / "abi_check.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <string.h>
+#include "bsattn.h"
+int main(void) {
+  attn_shape s;
+  memset(&s, 0, sizeof s);
+  s.batch = 1; s.num_q_heads = 32; s.num_kv_heads = 8; s.head_dim = 128;
+  s.block_q = 64; s.block_k = 64; s.q_len = 48384; s.q_valid = 48360;
+  s.kv_prefix_len = 512; s.kv_prefix_valid = 512; s.kv_len = 48896; s.kv_suffix_valid = 48360;
+  for (int i = 0; i < 3; ++i) {
+    const int64_t qs[3] = {48384LL * 32 * 128, 32 * 128, 128};
+    const int64_t ks[3] = {48896LL * 8 * 128, 8 * 128, 128};
+    s.q_stride[i] = qs[i]; s.o_stride[i] = qs[i]; s.k_stride[i] = ks[i]; s.v_stride[i] = ks[i];
+  }
+  printf("%d %d %d %zu %s\n", attn_keep_blocks(764, 8, 75), (int)attn_query_support(&s),
+         (int)ATTN_ERR_SELF_TEST, attn_select_workspace_size(&s), attn_version());
+  s.head_dim = 96;
+  const int st = (int)attn_query_support(&s);  /* before attn_last_error: C leaves
+                                                  the order of arguments open */
+  printf("%d %s\n", st, attn_last_error());
+  return 0;
+}
+""")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(bsa.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lbsattn",
+                    f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    first = out[0].split()
+    assert first[0] == "191" and first[1] == "0" and first[2] == "6"
+    assert int(first[3]) > 0 and first[4] == bsa.version()
+    assert out[1].startswith("2 attn_query_support: head_dim 96 unsupported")
