@@ -288,3 +288,27 @@ int main(void) {
     assert first[0] == "191" and first[1] == "0" and first[2] == "6"
     assert int(first[3]) > 0 and first[4] == bsa.version()
     assert out[1].startswith("2 attn_query_support: head_dim 96 unsupported")
+
+
+def test_last_error_is_per_thread():
+    """Each calling thread sees its own last failure."""
+    import threading
+    import synth
+    good = synth.make_case("thr", hq=2, hkv=1, d=64, prefix=64, gen=448, cfg=1).layout
+    bad = dict(good, head_dim=96)
+    results = {}
+    barrier = threading.Barrier(2)
+
+    def run(name, lay):
+        st = bsa.lib.attn_query_support(ctypes.byref(bsa.make_shape(lay)))
+        barrier.wait()  # both calls done before either thread reads its message
+        results[name] = (st, bsa.last_error())
+
+    ts = [threading.Thread(target=run, args=("bad", bad)),
+          threading.Thread(target=run, args=("good", good))]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    assert results["bad"][0] == 2 and "head_dim 96" in results["bad"][1]
+    assert results["good"] == (0, "")
