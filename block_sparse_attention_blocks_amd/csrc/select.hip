@@ -266,13 +266,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // Every product of two fp32 values is exact in fp64 and each accumulation is
 // rounded once, so the rigorous error bound of an fp64 dot product applies.
 // Phase 2: each wave takes rows and selects the top blocks by bisection on
-// the 32-bit keys, then writes the list in ascending block order. Eight
-// waves share both phases, which halves a workgroup's latency against four
-// (what decides the time when few heads give fewer workgroups than CUs).
-constexpr int kScoreWaves = 8;
-
-template <int D, int R>
-__global__ void __launch_bounds__(64 * kScoreWaves) score_topk_kernel(const ScoreParams p) {
+// the 32-bit keys, then writes the list in ascending block order. NW waves
+// share both phases: eight, or sixteen when the grid has fewer workgroups
+// than the chip has CUs (few heads), where a workgroup's latency is the
+// call's time.
+template <int D, int R, int NW>
+__global__ void __launch_bounds__(64 * NW) score_topk_kernel(const ScoreParams p) {
   extern __shared__ uint32_t keys_lds[];
   typedef double f64x4 __attribute__((ext_vector_type(4)));
   constexpr int KST = D / 4;  // MFMA k-steps over D
@@ -298,7 +297,7 @@ __global__ void __launch_bounds__(64 * kScoreWaves) score_topk_kernel(const Scor
     for (int st = 0; st < KST; ++st) qa[st] = qr[4 * st];
   }
   const int ntiles = (ncand + 15) >> 4;
-  for (int tile = wave; tile < ntiles; tile += kScoreWaves) {
+  for (int tile = wave; tile < ntiles; tile += NW) {
     const int c = tile * 16 + arow;  // candidate of this lane (B column, result column)
     const int j = p.n_prefix_blocks + min(c, ncand - 1);
     const float* kc = kcols + j + (int64_t)kq * p.nk;
@@ -331,7 +330,7 @@ __global__ void __launch_bounds__(64 * kScoreWaves) score_topk_kernel(const Scor
   // Exact recomputation of the marked scores (rare: a few in a hundred
   // thousand for typical inputs, but any number is handled), one whole wave
   // per score.
-  for (int e0 = wave * 64; e0 < nrows * ncp; e0 += 64 * kScoreWaves) {
+  for (int e0 = wave * 64; e0 < nrows * ncp; e0 += 64 * NW) {
     const int e = e0 + lane;
     uint64_t marked = __builtin_amdgcn_ballot_w64(e < nrows * ncp && keys_lds[e] == kUndecided);
     while (marked != 0) {
@@ -349,7 +348,7 @@ __global__ void __launch_bounds__(64 * kScoreWaves) score_topk_kernel(const Scor
   const bool take_all = rsel == ncand;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int M = ncp >> 6;
-  for (int r = wave; r < nrows; r += kScoreWaves) {
+  for (int r = wave; r < nrows; r += NW) {
     const int i = i0 + r;
     const int64_t row_id = ((int64_t)b * p.hq + h) * p.nq + i;
     int32_t* out = p.idx + row_id * p.idx_row_stride;
@@ -469,37 +468,38 @@ hipError_t launch_pool(const PoolParams& p, int head_dim, int batch, hipStream_t
   return hipGetLastError();
 }
 
+namespace {
+
+template <int D, int R, int NW>
+hipError_t launch_score_one(const ScoreParams& p, dim3 grid, size_t lds, hipStream_t stream) {
+  // Kernels taking more than 64 KiB of dynamic LDS must say so first.
+  static const hipError_t attr_status = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&score_topk_kernel<D, R, NW>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr_status != hipSuccess) return attr_status;
+  hipLaunchKernelGGL((score_topk_kernel<D, R, NW>), grid, dim3(64 * NW), lds, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int R>
+hipError_t launch_score_waves(const ScoreParams& p, dim3 grid, size_t lds, hipStream_t stream) {
+  const int64_t wgs = (int64_t)grid.x * grid.y * grid.z;
+  return wgs < 256 ? launch_score_one<D, R, 16>(p, grid, lds, stream)
+                   : launch_score_one<D, R, 8>(p, grid, lds, stream);
+}
+
+}  // namespace
+
 hipError_t launch_score_topk(const ScoreParams& p, int head_dim, int batch, hipStream_t stream) {
   const int rows = score_rows_per_wg(p.n_cand);
   const dim3 grid((p.nq + rows - 1) / rows, p.hq, batch);
   if (grid.x == 0) return hipSuccess;
   const size_t lds = score_lds_bytes(p.n_cand);
-  // Kernels taking more than 64 KiB of dynamic LDS must say so first.
-  static hipError_t attr_status = []() {
-    const int max_lds = 160 * 1024;
-    const void* fns[4] = {reinterpret_cast<const void*>(&score_topk_kernel<128, 16>),
-                          reinterpret_cast<const void*>(&score_topk_kernel<128, 8>),
-                          reinterpret_cast<const void*>(&score_topk_kernel<64, 16>),
-                          reinterpret_cast<const void*>(&score_topk_kernel<64, 8>)};
-    for (const void* f : fns) {
-      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-      if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-  }();
-  if (attr_status != hipSuccess) return attr_status;
-  if (head_dim == 128) {
-    if (rows == 16)
-      hipLaunchKernelGGL((score_topk_kernel<128, 16>), grid, dim3(64 * kScoreWaves), lds, stream, p);
-    else
-      hipLaunchKernelGGL((score_topk_kernel<128, 8>), grid, dim3(64 * kScoreWaves), lds, stream, p);
-  } else {
-    if (rows == 16)
-      hipLaunchKernelGGL((score_topk_kernel<64, 16>), grid, dim3(64 * kScoreWaves), lds, stream, p);
-    else
-      hipLaunchKernelGGL((score_topk_kernel<64, 8>), grid, dim3(64 * kScoreWaves), lds, stream, p);
-  }
-  return hipGetLastError();
+  if (head_dim == 128)
+    return rows == 16 ? launch_score_waves<128, 16>(p, grid, lds, stream)
+                      : launch_score_waves<128, 8>(p, grid, lds, stream);
+  return rows == 16 ? launch_score_waves<64, 16>(p, grid, lds, stream)
+                    : launch_score_waves<64, 8>(p, grid, lds, stream);
 }
 
 }  // namespace bsattn
