@@ -73,14 +73,25 @@ __global__ void __launch_bounds__(kPoolThreads) pool_kernel(const PoolParams p) 
   for (int e = 0; e < 8; ++e) acc[e] = 0.0;
   if (act) {
     const uint16_t* src = base + (int64_t)start * s1 + (int64_t)hh * s2 + dc * 8;
-#pragma unroll 8
-    for (int t = set; t < n; t += S) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)t * s1);
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    // Eight rows per turn, all eight loads issued before the first is used;
+    // rows past the block's real ones load nothing and add zeros (the sums
+    // stay exact).
+    for (int t0 = set; t0 < n; t0 += 8 * S) {
+      uint4 raw[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += (double)__uint_as_float(w[e] << 16);
-        acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
+      for (int x = 0; x < 8; ++x) {
+        const int t = t0 + x * S;
+        raw[x] = t < n ? *reinterpret_cast<const uint4*>(src + (int64_t)t * s1)
+                       : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const uint32_t w[4] = {raw[x].x, raw[x].y, raw[x].z, raw[x].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += (double)__uint_as_float(w[e] << 16);
+          acc[2 * e + 1] += (double)__uint_as_float(w[e] & 0xFFFF0000u);
+        }
       }
     }
   }
