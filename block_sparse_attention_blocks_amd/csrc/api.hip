@@ -63,6 +63,13 @@ int qparts_of(const attn_shape* s) { return s->block_q > 128 ? s->block_q / 128 
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Bytes from the first element of a (batch, head) slice of K or V to one
+// past its last: kv_len rows `row_stride` elements apart, head_dim each.
+int64_t kv_span_bytes(int32_t kv_len, int64_t row_stride, int32_t head_dim) {
+  if (kv_len <= 0) return 0;
+  return ((int64_t)(kv_len - 1) * row_stride + head_dim) * 2;
+}
+
 // Everything about the shape that the kernels rely on.
 attn_status validate_shape(const attn_shape* s, const char* fn) {
   if (s == nullptr) return fail(ATTN_ERR_INVALID_ARG, fn, "shape is NULL");
@@ -112,6 +119,15 @@ attn_status validate_shape(const attn_shape* s, const char* fn) {
     return fail(ATTN_ERR_INVALID_ARG, fn, "softmax_scale is not finite");
   if (s->batch > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, fn, "batch %d > 65535", s->batch);
+  // The attention kernel addresses one (batch, KV head) of K and V with
+  // 32-bit byte offsets and packs a block's first key row into 23 bits.
+  if (s->kv_len > (1 << 23))
+    return fail(ATTN_ERR_UNSUPPORTED, fn, "kv_len %d > %d", s->kv_len, 1 << 23);
+  if (kv_span_bytes(s->kv_len, s->k_stride[1], s->head_dim) > 0x7FFFFFFF ||
+      kv_span_bytes(s->kv_len, s->v_stride[1], s->head_dim) > 0x7FFFFFFF)
+    return fail(ATTN_ERR_UNSUPPORTED, fn,
+                "one KV head spans more than 2 GiB (kv_len %d, k row stride %lld, v row stride %lld)",
+                s->kv_len, (long long)s->k_stride[1], (long long)s->v_stride[1]);
   const int64_t nwg = (int64_t)s->batch * s->num_q_heads * (s->q_len / s->block_q) * qparts_of(s);
   // (+ up to 7 padding workgroups per (batch, KV head) in the head-synchronous order)
   if (nwg + 8 * (int64_t)s->batch * s->num_kv_heads > 0x7FFFFFFF)
@@ -250,6 +266,8 @@ attn_status run_attention(const char* fn, const attn_shape* s, const void* q, co
       (int64_t)s->batch * s->num_kv_heads * (int64_t)s->kv_len * s->head_dim * 2 * 2;
   p.head_sync = kv_bytes > ((int64_t)256 << 20) ? 1 : 0;
   p.scale_log2 = scale_of(s) * 1.4426950408889634f;
+  p.k_span_bytes = (uint32_t)kv_span_bytes(s->kv_len, s->k_stride[1], s->head_dim);
+  p.v_span_bytes = (uint32_t)kv_span_bytes(s->kv_len, s->v_stride[1], s->head_dim);
   if (p.n_wg == 0) return ok();
   st = check_device(fn);
   if (st != ATTN_OK) return st;

@@ -21,29 +21,40 @@
 // 256 registers, so every SIMD runs two waves (two 4-wave workgroups per CU
 // at 64-row blocks, one 8-wave workgroup at 128-row blocks; a 256-row block
 // runs as two 128-row workgroups on the same list); at head_dim 64 it needs
-// fewer than 168 and a SIMD runs three (three 64-row workgroups per CU).
-// While one wave waits (LDS, barrier, the HBM copies) another issues, and one
-// wave's softmax overlaps another's matrix products.
+// fewer than 168 and a SIMD runs three.
+//
+// What the main loop issues per wave and 64-key stage is kept to what the
+// matrix products need: on gfx950 every vector, scalar and LDS instruction a
+// SIMD issues between its matrix instructions costs matrix-core time, and so
+// does every wait on memory.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K fragment (A operand)
 //    comes from LDS, Q^T (B operand) stays in registers for the whole
-//    kernel. Each lane owns one query row and half of the 32 keys, so the
-//    row max needs a single cross-lane step.
-//  * Online softmax in fp32 in the log2 domain, the scale folded into one
-//    FMA; the reference max of a row moves only when a stage max exceeds it
-//    by more than 2^8 (lazy rescale), and the cross-lane step is skipped when
-//    no lane comes near that. Row sums are accumulated on the vector ALU.
+//    kernel. Each lane owns one query row and half of the wave's 32 keys.
+//  * Online softmax in fp32 in the log2 domain, the scale folded into the
+//    exponential's FMA. A row's reference maximum moves only when a stage
+//    maximum exceeds it by more than 2^8 (lazy rescale); the per-stage test
+//    is one compare against a precomputed threshold, and everything else
+//    (the cross-lane maximum, the rescale of the running output) runs only
+//    when some lane trips it, which after the first stages is rare. Row sums
+//    add the fp32 probabilities in two independent chains.
 //  * O^T = V^T P^T with the same MFMA: P^T is the S^T accumulator converted
-//    to bf16 in place (the contraction over keys is order-free, so the key
-//    order of the accumulator layout is reused for V); V^T fragments come
-//    from the row-major V tile through ds_read_b64_tr_b16.
+//    to bf16 (the contraction over keys is order-free, so the key order of
+//    the accumulator layout is reused for V); V^T fragments come from the
+//    row-major V tile through ds_read_b64_tr_b16.
 //  * Inside a wave the QK^T MFMAs of the next stage are interleaved with the
 //    exponentials of the current one, and the PV MFMAs with the row maxima
 //    of the next.
-//  * K and V stages move HBM -> LDS with global_load_lds_dwordx4 (no VGPR
-//    staging), XOR-swizzled in 16-byte chunks so that the K row reads and
-//    the V transpose reads hit distinct banks, double buffered: K two stages
-//    ahead, V one. One workgroup barrier per stage. Past the end of the list
-//    the copies keep running on in-bounds rows, so they need no branch.
+//  * K and V stages move HBM -> LDS with buffer_load_dwordx4 ... lds (no
+//    VGPR staging): the buffer resource of the (batch, KV head) and each
+//    lane's offset are fixed, the stage enters as one scalar byte offset.
+//    Rows are XOR-swizzled in 16-byte chunks so the K row reads and the V
+//    transpose reads hit distinct banks. K is copied KR - 1 stages ahead of
+//    its use (a ring of KR stages), V one stage ahead (two stages), so a
+//    stage's wait leaves the newest K copies in flight. One workgroup
+//    barrier per stage.
+//  * The block list is read 64 entries per vector load; each entry becomes a
+//    descriptor (first key row, real keys in the block) once, and a stage
+//    takes its descriptor with one v_readlane.
 //  * Workgroups are renumbered so that each XCD works through a contiguous
 //    range of (KV head, query block), keeping that range's K/V tiles in the
 //    XCD's L2.
@@ -60,6 +71,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
 // Chunk permutation of row `row` in an LDS tile with CPR 16-byte chunks.
 // LDS serves 256 contiguous bytes per cycle. With 16 chunks per row (head
@@ -91,70 +103,13 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Workgroup barrier that orders LDS accesses only. Unlike __syncthreads()
 // it does not wait for outstanding HBM->LDS copies, which stay in flight
-// across it; their completion is awaited explicitly with wait_vmcnt.
+// across it; their completion is awaited explicitly with wait_vmcnt. The
+// empty asm statements keep the compiler from moving memory operations
+// (the copies included) across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// HBM->LDS copy of this wave's RPW rows (rows RPW w .. RPW w + RPW - 1) of a
-// 64-row stage, with global_load_lds_dwordx4 in its scalar-base form: the LDS
-// destination comes from M0 and the HBM address is a 64-bit scalar base plus
-// a 32-bit per-lane offset, so a copy costs no vector ALU work. Instruction
-// `it` moves 64 x 16 bytes = RPI whole rows. The lane's chunk within its row
-// carries the XOR swizzle, which depends on the row modulo 16 only.
-//
-// The copies are issued from inline assembly, so the compiler does not track
-// them: every read of a stage is preceded by an explicit wait_vmcnt and a
-// workgroup barrier.
-template <int D, int RPW>
-struct StageCopy {
-  static constexpr int CPR = D / 8;
-  static constexpr int RPI = 64 / CPR;
-  static constexpr int NL = RPW / RPI;  // instructions per wave and stage
-  static_assert(NL * RPI == RPW && NL >= 1, "rows per wave");
-  uint32_t voff[NL];                   // per-lane byte offsets
-
-  // The swizzle follows the row's position in the stage (RPW wave + row).
-  __device__ __forceinline__ void init(int64_t row_stride, int lane, int wave) {
-#pragma unroll
-    for (int it = 0; it < NL; ++it) {
-      const int row = it * RPI + lane / CPR;
-      const int lch = (lane % CPR) ^ swz<CPR>(wave * RPW + row);
-      voff[it] = (uint32_t)((row * row_stride + lch * 8) * 2);
-    }
-  }
-  template <int IT>
-  __device__ __forceinline__ void one(const uint16_t* rows, uint32_t lds) const {
-    asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :
-                 : "v"(voff[IT]), "s"(rows), "s"(lds), "i"(IT * 1024)
-                 : "memory", "m0");
-  }
-  // `rows`: uniform address of this wave's first row; `lds`: LDS byte address
-  // of this wave's part of the stage. `it` is a constant after unrolling.
-  __device__ __forceinline__ void issue_one(int it, const uint16_t* rows, uint32_t lds) const {
-    switch (it) {
-      case 0: one<0>(rows, lds); break;
-      case 1: one<1 % NL>(rows, lds); break;
-      case 2: one<2 % NL>(rows, lds); break;
-      case 3: one<3 % NL>(rows, lds); break;
-      default: break;
-    }
-  }
-  __device__ __forceinline__ void issue(const uint16_t* rows, uint32_t lds) const {
-#pragma unroll
-    for (int it = 0; it < NL; ++it) issue_one(it, rows, lds);
-  }
-};
-
-// Uniform 32-bit load through the scalar data cache (the index list is
-// read-only here); waits for its own completion.
-__device__ __forceinline__ int scalar_load_i32(const int32_t* ptr) {
-  int v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-  return v;
 }
 
 // Lanes l and l ^ 32 hold the same query row (different keys).
@@ -173,11 +128,17 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// K stages in LDS. Two (K copied one stage ahead, like V) keep the main loop
+// within 256 registers; a ring of three needs the loop unrolled six stages
+// deep, and the longer live ranges then spill the Q fragments.
+template <int D, int NQG>
+constexpr int k_ring() { return 2; }
+
 template <int D, int BK, int NQG, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ smem) {
   constexpr bool DENSE = MODE != kSparse;    // the list is every non-empty block
   constexpr bool CAUSAL = MODE == kCausal;   // ... cut to the causal range
-  constexpr int CPR = D / 8;
+  constexpr int CPR = D / 8;     // 16-byte chunks per K/V row
   constexpr int KS = D / 16;     // MFMA k-steps over D (QK^T MFMAs per stage)
   constexpr int DT = D / 32;     // output 32-row tiles over D
   constexpr int SPB = BK / 64;   // 64-key stages per block
@@ -185,7 +146,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   static_assert(SPB == 1 || SPB == 2, "block_k 64 or 128");
   constexpr int NW = 2 * NQG;    // waves: NQG query groups of 32 rows x 2 key halves
   constexpr int RPW = 64 / NW;   // stage rows copied by each wave
-  using Copy = StageCopy<D, RPW>;
+  constexpr int RPI = 64 / CPR;  // rows moved by one copy instruction (64 lanes x 16 bytes)
+  constexpr int NL = RPW / RPI;  // copy instructions per wave for one K (or V) stage
+  static_assert(NL >= 1 && NL * RPI == RPW, "rows per wave");
+  constexpr int KR = k_ring<D, NQG>();    // K stages in LDS (K is copied KR - 1 stages ahead)
+  constexpr int PERIOD = KR % 2 ? 2 * KR : KR;  // steps after which every buffer index repeats
   // A row moves its reference max only when a stage max exceeds it by more
   // than this many powers of two; until then probabilities are taken against
   // the stale max and stay below 2^8, far from fp32 or bf16 overflow.
@@ -233,7 +198,6 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int row0 = (i * p.qparts + part) * (32 * NQG);
   const int qrow = row0 + 32 * qh + col;
 
-
   int nblk;
   const int32_t* idx_row = nullptr;
   if constexpr (CAUSAL) {
@@ -253,7 +217,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     nblk = p.n_forced + p.n_cand;
   } else {
     const int64_t row_id = ((int64_t)b * p.hq + h) * p.nq + i;
-    nblk = min(max(scalar_load_i32(p.cnt + row_id), 0), p.idx_row_stride);
+    nblk = min(max(__builtin_amdgcn_readfirstlane(p.cnt[row_id]), 0), p.idx_row_stride);
     idx_row = p.idx + row_id * p.idx_row_stride;
   }
   if (row0 >= p.q_valid || p.nk == 0) nblk = 0;
@@ -269,24 +233,56 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   // bitwise reproducible.
   const int cohort = (w >> 8) % (D == 64 ? 3 : 2);  // (w / 8) / 32: cohorts of 32 per XCD
   const int n_first = (NQG == 2) ? (cohort * nblk) / (D == 64 ? 3 : 2) : 0;
-  // The list, 64 positions at a time: lane l of lw_cur holds list position
-  // 64 lw_c + l (after the rotation), lw_next the next 64. Each chunk is one
-  // vector load issued a whole chunk before its first use, so reading the
-  // list never waits on memory.
-  int lw_cur = -1, lw_next = -1, lw_c = 0;
+
+  // Block j as a descriptor: (first key row << 8) | real keys in the block,
+  // 0 for an entry outside [0, NK) (copied from block 0, every key masked).
+  // Real keys of a block form a prefix of it: segments are block aligned and
+  // padding follows the real keys of each segment.
+  auto desc_of_block = [&](int j) -> int {
+    const int s0 = j * BK;
+    const int seg_end =
+        (s0 < p.kv_prefix_len) ? p.kv_prefix_valid : p.kv_prefix_len + p.kv_suffix_valid;
+    const int nv = min(max(seg_end - s0, 0), BK);
+    return (j < 0 || j >= p.nk) ? 0 : ((s0 << 8) | nv);
+  };
+  // The list, 64 positions at a time: lane l of lw_cur holds the descriptor
+  // of list position 64 c + l (after the rotation) for the current chunk c;
+  // lw_raw holds the raw entries of chunk c + 1, loaded a whole chunk ahead
+  // (unconditionally, from a position clamped into the list, so that the
+  // load lands in its own register and nothing waits for it until the
+  // chunk is used; positions past the end are dropped at that point).
+  int lw_cur = 0, lw_raw = -1, lw_c = 0;
   auto load_chunk = [&](int c) -> int {
-    const int pos = c * 64 + lane;
-    int n = pos + n_first;
+    int n = min(c * 64 + lane, nblk - 1) + n_first;
     if (n >= nblk) n -= nblk;
-    return pos < nblk ? idx_row[n] : -1;
+    return idx_row[n];
+  };
+  auto chunk_desc = [&](int raw, int c) {
+    return desc_of_block(c * 64 + lane < nblk ? raw : -1);
   };
   if constexpr (!DENSE) {
-    lw_cur = load_chunk(0);
-    lw_next = load_chunk(1);
+    if (nblk > 0) {
+      lw_cur = chunk_desc(load_chunk(0), 0);
+      lw_raw = load_chunk(1);
+    }
   }
+  // Descriptor of list position n_pos (positions are asked for in order).
+  auto block_desc = [&](int n_pos) -> int {
+    if constexpr (DENSE) {
+      int n = n_pos + n_first;
+      if (n >= nblk) n -= nblk;
+      return desc_of_block(n < p.n_forced ? n : p.n_prefix_blocks + (n - p.n_forced));
+    } else {
+      if ((n_pos >> 6) != lw_c) {  // next chunk (uniform, once per 64 positions)
+        ++lw_c;
+        lw_cur = chunk_desc(lw_raw, lw_c);
+        lw_raw = load_chunk(lw_c + 1);
+      }
+      return __builtin_amdgcn_readlane(lw_cur, n_pos & 63);
+    }
+  };
+
   // Q^T fragments (B operand): the lane holds q[qrow][16 ks + 8 half .. +7].
-  // Issued after the list's first chunks (whose first use waits only for
-  // those) and awaited together with the first stage copies.
   bf16x8 qf[KS];
   {
     const uint16_t* qp =
@@ -295,50 +291,47 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     for (int ks = 0; ks < KS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
 
+  // Copies: one buffer resource per (batch, KV head) for K and for V, a fixed
+  // per-lane byte offset per copy instruction (row within the stage and
+  // swizzled chunk), and the stage's first key row as a scalar byte offset.
   const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
   const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
-  Copy kcopy, vcopy;
-  kcopy.init(p.ks1, lane, wave);
-  vcopy.init(p.vs1, lane, wave);
-  // LDS: K stages 0, 1 then V stages 0, 1; this wave copies rows RPW wave ..
-  const uint32_t smem_addr =
-      (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) uint16_t*)smem);
-  const uint32_t wcopy = (uint32_t)(wave * RPW * D * 2);
-  auto k_stage = [&](int s) { return smem_addr + (uint32_t)(s * STAGE * 2) + wcopy; };
-  auto v_stage = [&](int s) { return smem_addr + (uint32_t)((2 + s) * STAGE * 2) + wcopy; };
-
-  // Listed block n. Entries outside [0, NK) are copied from block 0 (always
-  // in bounds) with no real key, which gives them zero weight.
-  auto block_of = [&](int n_pos) -> int {
-    int n = n_pos + n_first;
-    if (n >= nblk) n -= nblk;
-    if constexpr (DENSE) {
-      return n < p.n_forced ? n : p.n_prefix_blocks + (n - p.n_forced);
-    } else {
-      return __builtin_amdgcn_readlane(lw_cur, n_pos & 63);  // n_pos lies in chunk lw_c
-    }
+  const auto krsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0,
+                                                       p.k_span_bytes, 0x00020000);
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0,
+                                                       p.v_span_bytes, 0x00020000);
+  const int krow_b = (int)p.ks1 * 2, vrow_b = (int)p.vs1 * 2;  // bytes per key row
+  int kvoff[NL], vvoff[NL];
+#pragma unroll
+  for (int it = 0; it < NL; ++it) {
+    const int row = wave * RPW + it * RPI + lane / CPR;  // row within the stage
+    const int gch = (lane % CPR) ^ swz<CPR>(row);         // chunk this lane's LDS slot holds
+    kvoff[it] = row * krow_b + gch * 16;
+    vvoff[it] = row * vrow_b + gch * 16;
+  }
+  lds_u16* const lds = (lds_u16*)smem;
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
+  // LDS: K stages 0 .. KR - 1, then V stages 0, 1. A copy instruction writes
+  // 64 lanes x 16 bytes from M0 on, rows RPW wave + RPI it .. of its stage.
+  // The copies are issued from inline assembly: the compiler then neither
+  // counts them nor orders LDS reads behind them (it cannot tell that they
+  // write other stages than the ones being read), so every read of a stage
+  // is preceded by an explicit wait_vmcnt and a workgroup barrier.
+  auto copy_one = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t m0, int voff, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "m0");
   };
-  // Real keys of block j form a prefix [0, nvalid) of the block: segments
-  // are block aligned and padding follows the real keys of each segment.
-  auto nvalid_of = [&](int j) -> int {
-    if (j < 0 || j >= p.nk) return 0;
-    const int s0 = j * BK;
-    const int seg_end =
-        (s0 < p.kv_prefix_len) ? p.kv_prefix_valid : p.kv_prefix_len + p.kv_suffix_valid;
-    return min(max(seg_end - s0, 0), BK);
+  auto copy_k = [&](auto kb_c, int it, int row) {
+    constexpr int KB = decltype(kb_c)::value;
+    copy_one(krsrc, lds_addr + (uint32_t)((KB * STAGE + (wave * RPW + it * RPI) * D) * 2),
+             kvoff[it], row * krow_b);
   };
-  // First HBM row copied by this wave for stage x of block j.
-  auto copy_row_of = [&](int j, int x) -> int64_t {
-    return ((j < 0 || j >= p.nk) ? 0 : (int64_t)j * BK) + (x % SPB) * 64 + wave * RPW;
-  };
-  // Real keys among this wave's 32 keys of stage x of a block with nv real keys.
-  auto nvs_of = [&](int nv, int x) { return min(max(nv - (x % SPB) * 64 - kh * 32, 0), 32); };
-  // Rank among the real keys of the first of this wave's 32 keys of stage x
-  // of block j (causal mode; blocks are segment aligned and real keys lead
-  // each segment).
-  auto rank0_of = [&](int j, int x) {
-    const int k0 = j * BK + (x % SPB) * 64 + 32 * kh;
-    return j < p.n_prefix_blocks ? k0 : p.kv_prefix_valid + (k0 - p.kv_prefix_len);
+  auto copy_v = [&](auto vb_c, int it, int row) {
+    constexpr int VB = decltype(vb_c)::value;
+    copy_one(vrsrc, lds_addr + (uint32_t)(((KR + VB) * STAGE + (wave * RPW + it * RPI) * D) * 2),
+             vvoff[it], row * vrow_b);
   };
 
   f32x16 o[DT];
@@ -347,35 +340,67 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
   const float sl2 = p.scale_log2;
+  const float inv_sl2 = 1.0f / sl2;
 
   // LDS element offsets (within a stage) that do not depend on the stage.
   const int sw = swz<CPR>(col);  // swizzle of K row 32 kh + col
   int koffs[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) koffs[ks] = (32 * kh + col) * D + (((2 * ks + half) ^ sw) << 3);
+  // V^T reads: LDS byte address of the lane's fragment in V stage 0. The V
+  // stages lie above the K ring, past 64 KB for the second one; the base is
+  // hidden from the compiler's constant folding so that both stages (and
+  // both key steps) are immediate offsets from these registers.
   const int g16 = lane >> 4, j16 = lane & 15, tq = j16 >> 2, q4 = j16 & 3;
-  int voffs[DT][2];
+  int vrd[DT][2];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       const int d = dt * 32 + 16 * (g16 & 1) + 4 * q4;
       const int row = 8 * c2 + 4 * half + tq;  // + 32 kh + 16 per key step
-      voffs[dt][c2] = (32 * kh + row) * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7);
+      vrd[dt][c2] =
+          (KR * STAGE + (32 * kh + row) * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7)) * 2;
+      asm volatile("" : "+v"(vrd[dt][c2]));
     }
+  typedef __attribute__((address_space(3))) char lds_char;
+  auto vread = [&](int vb_stage, int ks2, int dt, int c2) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)((lds_char*)lds + vrd[dt][c2] + (vb_stage * STAGE + 16 * ks2 * D) * 2));
+  };
 
   // Softmax state of this lane's query row over this wave's keys.
   float m_run = -__builtin_inff();  // reference max (log2 units)
   float m_use = 0.0f;               // m_run, or 0 while it is -inf
-  float alpha = 1.0f;
+  float thr = -__builtin_inff();    // raw-score threshold: (m_run + slack) / scale
   float lsum = 0.0f;                // this lane's part of the row sum, relative to m_use
-  bool need = false;
+
+  // Stage descriptors: first key row of the stage and real keys among its 64.
+  // SUB is the stage's 64-key part of its block (x % SPB, a compile-time
+  // value at every call). Stages past the end of the list keep the previous
+  // descriptor: their copies land in buffers that are not read again.
+  int blk_desc = 0;
+  auto stage_desc = [&](auto sub_c, int x, int& row, int& nv) {
+    constexpr int SUB = decltype(sub_c)::value;
+    if (x < nst) {
+      if constexpr (SUB == 0) blk_desc = block_desc(x / SPB);
+      row = (blk_desc >> 8) + SUB * 64;
+      nv = min(max((blk_desc & 255) - SUB * 64, 0), 64);
+    }
+  };
+
   // Keys of the wave's 32 at or past `nvs` are padding. In causal mode key
   // kk also has rank rank0 + kk, and row qrow keeps ranks <= qrow + causal_off.
-  auto mask = [&](f32x16& sd, int nvs, int rank0) {
-    int lim = nvs;      // this lane keeps keys [0, lim)
+  auto rank0_of = [&](int row) {
+    const int k0 = row + 32 * kh;
+    return k0 < p.kv_prefix_len ? k0 : p.kv_prefix_valid + (k0 - p.kv_prefix_len);
+  };
+  auto mask = [&](f32x16& sd, int nv, int row) {
+    const int nvs = min(max(nv - 32 * kh, 0), 32);
+    int lim = nvs;  // this lane keeps keys [0, lim)
     bool any = nvs < 32;
     if constexpr (CAUSAL) {
+      const int rank0 = rank0_of(row);
       lim = min(nvs, qrow + p.causal_off - rank0 + 1);
       any = any || (row0 + 32 * qh + p.causal_off - rank0 + 1 < 32);  // the wave's first row
     }
@@ -387,198 +412,218 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       }
     }
   };
-  // Reference update from the lane's partial row maximum of a fresh S.
-  auto prep_tail = [&](float mxl) {
-    // When no lane's partial maximum clears its row's reference by the slack,
-    // neither does any row maximum and nothing changes (the usual case after
-    // the first stages): the cross-lane step is skipped.
-    float mx = -__builtin_inff();
-    if (__builtin_amdgcn_ballot_w64(mxl * sl2 > m_run + kRescaleSlack) != 0)
-      mx = max_with_other_half(mxl) * sl2;
-    const bool moves = mx > m_run + kRescaleSlack;
-    // While the reference is -inf no key has contributed: nothing to rescale.
-    need = moves && m_run != -__builtin_inff();
-    const float e_alpha = __builtin_amdgcn_exp2f(m_run - mx);
-    alpha = need ? e_alpha : 1.0f;
-    m_run = moves ? mx : m_run;
-    m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
-  };
-  auto prep = [&](const f32x16& sd) {
-    float mxl = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(sd[r], sd[r + 1]));
-    prep_tail(mxl);
-  };
-
-  // Blocks around the current stage u (in block n = u / SPB):
-  // (j0, nv0) block n, (j1, nv1) block n + 1, (j2, nv2) block n + 2.
-  int j0 = -1, nv0 = 0, j1 = -1, nv1 = 0, j2 = -1, nv2 = 0;
-  f32x16 sA, sB;
-
-  if (nst > 0) {
-    j0 = block_of(0);
-    nv0 = nvalid_of(j0);
-    if (nblk > 1) {
-      j1 = block_of(1);
-      nv1 = nvalid_of(j1);
-    }
-    kcopy.issue(kbase + copy_row_of(j0, 0) * p.ks1, k_stage(0));
-    vcopy.issue(vbase + copy_row_of(j0, 0) * p.vs1, v_stage(0));
-    if (nst > 1) {
-      const int jn = (SPB == 1) ? j1 : j0;
-      kcopy.issue(kbase + copy_row_of(jn, 1) * p.ks1, k_stage(1));
-    }
-    wait_vmcnt<0>();
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sA[r] = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + koffs[ks]);
-      sA = mfma(a, qf[ks], sA);
-    }
-    mask(sA, nvs_of(nv0, 0), CAUSAL ? rank0_of(j0, 0) : 0);
-    prep(sA);
-  }
-
-  // One pipeline step on stage u. KP: the K stage read in this step (that of
-  // stage u + 1); VP: the V stage (that of stage u). Copies issued here: V of
-  // u + 1 into V stage VP ^ 1 and K of u + 2 into K stage KP ^ 1; both were
-  // last read in the previous step, which every wave has left at the barrier.
-  auto step = [&](auto kp_c, auto vp_c, int u, f32x16& s_cur, f32x16& s_nxt) {
-    constexpr int KP = decltype(kp_c)::value;
-    constexpr int VP = decltype(vp_c)::value;
-    const bool last_sub = (u % SPB) == SPB - 1;
-    const int n = u / SPB;
-    if (last_sub) {
-      if constexpr (!DENSE) {
-        if (n + 2 < nblk && ((n + 2) & 63) == 0) {
-          lw_cur = lw_next;
-          ++lw_c;
-          lw_next = load_chunk(lw_c + 1);
-        }
-      }
-      j2 = (n + 2 < nblk) ? block_of(n + 2) : -1;
-      nv2 = (n + 2 < nblk) ? nvalid_of(j2) : 0;
-    }
-    // ---- the step's single synchronisation point.
-    wait_vmcnt<0>();
-    lds_barrier();
-    // Past the end of the list the copies still run (their slots are never
-    // read again, or only by the masked dummy product) but read this head's
-    // first rows, which are always in bounds: no branch per copy.
-    const bool v_next = u + 1 < nst, k_next = u + 2 < nst;
-    const uint16_t* v_rows =
-        v_next ? vbase + copy_row_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) * p.vs1
-               : vbase + (int64_t)wave * RPW * p.vs1;
-    const uint16_t* k_rows =
-        k_next ? kbase + copy_row_of((SPB == 1) ? j2 : j1, u + 2) * p.ks1
-               : kbase + (int64_t)wave * RPW * p.ks1;
-    const uint16_t* kb = smem + KP * STAGE;
-    uint16_t* vb = smem + (2 + VP) * STAGE;
-    const int nvs = nvs_of(nv0, u);
-    if (nvs < 32) {
-      // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows
-      // (both waves of this key half write the same zeros).
-      uint4* vz = reinterpret_cast<uint4*>(vb + (32 * kh + nvs) * D);
-      const int nz = (32 - nvs) * D / 8;
-      for (int e = lane; e < nz; e += 64) vz[e] = make_uint4(0, 0, 0, 0);
-    }
-    // Lazy rescale of the running output (rare after the first stages).
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+  // Lazy rescale: `mxl` is the lane's maximum raw score over its keys of the
+  // newest stage. One compare per stage; the rest only when a lane trips it.
+  auto check_ref = [&](float mxl) {
+    if (__builtin_amdgcn_ballot_w64(mxl > thr) != 0) {
+      const float mx = max_with_other_half(mxl) * sl2;
+      const bool moves = mx > m_run + kRescaleSlack;
+      // While the reference is -inf no key has contributed: nothing to rescale.
+      const float alpha =
+          (moves && m_run != -__builtin_inff()) ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;
+      m_run = moves ? mx : m_run;
+      m_use = (m_run == -__builtin_inff()) ? 0.0f : m_run;
+      thr = (m_run + kRescaleSlack) * inv_sl2;
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
     }
+  };
+  auto row_max = [&](const f32x16& sd) {
+    float mxl = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(sd[r], sd[r + 1]));
+    return mxl;
+  };
+
+  // Descriptors of the stages in the pipeline: before step u, index x holds
+  // stage u + x (x < KR); the step shifts them, so that index x then holds
+  // stage u + 1 + x and the new stage u + KR enters at index KR - 1.
+  int srow[KR], snv[KR];
+#pragma unroll
+  for (int x = 0; x < KR; ++x) srow[x] = snv[x] = 0;
+  f32x16 sbuf[2];
+
+  if (nst > 0) {
+    // Prologue: K of stages 0 .. KR - 1 and V of stage 0, then S[0].
+    stage_desc(std::integral_constant<int, 0>{}, 0, srow[0], snv[0]);
+#pragma unroll
+    for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, 0>{}, it, srow[0]);
+#pragma unroll
+    for (int it = 0; it < NL; ++it) copy_v(std::integral_constant<int, 0>{}, it, srow[0]);
+    srow[1] = srow[0];
+    snv[1] = snv[0];
+    stage_desc(std::integral_constant<int, 1 % SPB>{}, 1, srow[1], snv[1]);
+#pragma unroll
+    for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, 1>{}, it, srow[1]);
+    if constexpr (KR == 3) {
+      srow[2] = srow[1];
+      snv[2] = snv[1];
+      stage_desc(std::integral_constant<int, 2 % SPB>{}, 2, srow[2], snv[2]);
+#pragma unroll
+      for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, 2>{}, it, srow[2]);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sbuf[0][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(smem + koffs[ks]);
+      sbuf[0] = mfma(a, qf[ks], sbuf[0]);
+    }
+    mask(sbuf[0], snv[0], srow[0]);
+    check_ref(row_max(sbuf[0]));
+  }
+  static_assert(KR == 2 || KR == 3, "K ring of two or three stages");
+
+  // One pipeline step on stage u (step S of the period, u % PERIOD == S).
+  // K stage u + 1 is read from K buffer (S + 1) % KR, V stage u from V buffer
+  // S % 2; the step copies V of u + 1 into V buffer (S + 1) % 2 and K of
+  // u + KR into K buffer S % KR. Both were last read in the previous step,
+  // which every wave has left at the barrier. LAST: stage u is the last one
+  // (no S[u+1] and no copies).
+  int cur_nv = snv[0];  // real keys of the current stage
+  auto run_step = [&](auto s_c, int u, auto last_c) {
+    constexpr int S = decltype(s_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    constexpr int KB = (S + 1) % KR, VB = S % 2;
+    constexpr int KNEW = S % KR, VNEW = (S + 1) % 2;
+    f32x16& s_cur = sbuf[S % 2];
+    f32x16& s_nxt = sbuf[(S + 1) % 2];
+    if constexpr (!LAST) {
+      // Index x now holds stage u + 1 + x; stage u + KR enters at KR - 1.
+#pragma unroll
+      for (int x = 0; x + 1 < KR; ++x) {
+        srow[x] = srow[x + 1];
+        snv[x] = snv[x + 1];
+      }
+      stage_desc(std::integral_constant<int, (S + KR) % SPB>{}, u + KR, srow[KR - 1],
+                 snv[KR - 1]);
+    }
+    // ---- the step's single synchronisation point: V of u and K of u + 1
+    // have landed; with a ring of three K stages the copies of K of u + 2
+    // (issued last) may still be in flight.
+    if constexpr (LAST || KR == 2) {
+      wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<NL>();
+    }
+    lds_barrier();
+    const uint16_t* kb = smem + KB * STAGE;
+    uint16_t* vb = smem + (KR + VB) * STAGE;
+    {
+      const int nvs = min(max(cur_nv - 32 * kh, 0), 32);
+      if (nvs < 32) {
+        // Padded keys get weight 0, but 0 * NaN is NaN: clear their V rows
+        // (both waves of this key half write the same zeros).
+        uint4* vz = reinterpret_cast<uint4*>(vb + (32 * kh + nvs) * D);
+        const int nz = (32 - nvs) * D / 8;
+        for (int e = lane; e < nz; e += 64) vz[e] = make_uint4(0, 0, 0, 0);
+      }
+    }
 
     // ---- (a) S[u+1] = K Q^T || exponentials of P[u] || V^T reads || copies.
     bf16x8 pf[2];
-    bf16x4 vf[2][DT][2];
+    // V^T fragments of the first 16 keys are read during (a), those of the
+    // second 16 during the first PV products of (b) (into registers the
+    // consumed S[u] leaves free).
+    bf16x4 vf0[DT][2], vf1[DT][2];
     constexpr int EXP_PER = 16 / KS;  // exponentials per MFMA slot
-    constexpr int NVRD = 2 * DT * 2;  // V^T reads of the step
+    constexpr int NVRD = DT * 2;      // V^T reads of (a)
     constexpr int VRD_PER = NVRD / KS;
-    static_assert(NVRD % KS == 0, "V reads per slot");
+    static_assert(NVRD % KS == 0 && EXP_PER % 2 == 0, "slots");
+    constexpr int NCOPY = 2 * NL;     // copy instructions of the step
+    static_assert(KS % NCOPY == 0, "copy slots");
+    constexpr int CEVERY = KS / NCOPY;
     bf16x8 kf[3];
-    kf[0] = *reinterpret_cast<const bf16x8*>(kb + koffs[0]);
-    kf[1] = *reinterpret_cast<const bf16x8*>(kb + koffs[1]);
+    float lsa = 0.0f, lsb = 0.0f;  // row sum of the stage's probabilities (fp32)
+    if constexpr (!LAST) {
+      kf[0] = *reinterpret_cast<const bf16x8*>(kb + koffs[0]);
+      kf[1] = *reinterpret_cast<const bf16x8*>(kb + koffs[1]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
+    }
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      if (k + 2 < KS) kf[(k + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + koffs[k + 2]);
-      s_nxt = mfma(kf[k % 3], qf[k], s_nxt);
-      // The copy instructions spread evenly over the slots (V of u + 1, then
-      // K of u + 2).
-      static_assert(KS % (2 * Copy::NL) == 0, "copy slots");
-      constexpr int CEVERY = KS / (2 * Copy::NL);
-      if (k % CEVERY == 0) {
-        const int c = k / CEVERY;
-        if (c < Copy::NL) {
-          vcopy.issue_one(c, v_rows, v_stage(VP ^ 1));
-        } else {
-          kcopy.issue_one(c - Copy::NL, k_rows, k_stage(KP ^ 1));
+      if constexpr (!LAST) {
+        if (k + 2 < KS) kf[(k + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + koffs[k + 2]);
+        s_nxt = mfma(kf[k % 3], qf[k], s_nxt);
+        // The copy instructions spread evenly over the slots (V of u + 1,
+        // then K of u + KR).
+        if (k % CEVERY == 0) {
+          const int c = k / CEVERY;
+          if (c < NL) {
+            copy_v(std::integral_constant<int, VNEW>{}, c, srow[0]);
+          } else {
+            copy_k(std::integral_constant<int, KNEW>{}, c - NL, srow[KR - 1]);
+          }
         }
       }
 #pragma unroll
-      for (int x = 0; x < EXP_PER; ++x) {
+      for (int x = 0; x < EXP_PER; x += 2) {
         const int r = k * EXP_PER + x;
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], sl2, -m_use));
-        // Pin the exponential to this slot: without it the compiler sinks
+        float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r], sl2, -m_use));
+        float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[r + 1], sl2, -m_use));
+        // Pin the exponentials to this slot: without it the compiler sinks
         // the softmax below the masking branch, after every QK^T MFMA.
-        asm volatile("" : "+v"(e));
-        lsum += e;
-        pf[r / 8][r % 8] = (__bf16)e;
+        asm volatile("" : "+v"(e0), "+v"(e1));
+        pf[r / 8][r % 8] = (__bf16)e0;
+        pf[r / 8][r % 8 + 1] = (__bf16)e1;
+        lsa += e0;
+        lsb += e1;
       }
 #pragma unroll
       for (int x = 0; x < VRD_PER; ++x) {
         const int idx = k * VRD_PER + x;
-        const int ks2 = idx / (DT * 2), dt = (idx / 2) % DT, c2 = idx % 2;
-        vf[ks2][dt][c2] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-            (lds_bf16x4*)(vb + 16 * ks2 * D + voffs[dt][c2]));
+        const int dt = idx / 2, c2 = idx % 2;
+        vf0[dt][c2] = vread(VB, 0, dt, c2);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    lsum += lsa + lsb;
 
-    // With no next stage, S[u+1] is a dummy product and every key of it
-    // counts as padding, which leaves the softmax state unchanged.
-    const int nvs_next = (u + 1 < nst) ? nvs_of((SPB == 1 || last_sub) ? nv1 : nv0, u + 1) : 0;
-    mask(s_nxt, nvs_next,
-         CAUSAL ? rank0_of((SPB == 1 || last_sub) ? j1 : j0, u + 1) : 0);
+    if constexpr (!LAST) mask(s_nxt, u + 1 < nst ? snv[0] : 0, srow[0]);
     // ---- (b) O += V^T P[u]^T || row max of S[u+1].
     float mxl = -__builtin_inff();
     constexpr int NPV = 2 * DT;
 #pragma unroll
     for (int sl = 0; sl < NPV; ++sl) {
       const int ks2 = sl / DT, dt = sl % DT;
-      const bf16x8 av =
-          __builtin_shufflevector(vf[ks2][dt][0], vf[ks2][dt][1], 0, 1, 2, 3, 4, 5, 6, 7);
-      o[dt] = mfma(av, pf[ks2], o[dt]);
+      if (sl < DT) {
 #pragma unroll
-      for (int it = sl * 8 / NPV; it < (sl + 1) * 8 / NPV; ++it) {
-        mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(s_nxt[2 * it], s_nxt[2 * it + 1]));
-        asm volatile("" : "+v"(mxl));
+        for (int c2 = 0; c2 < 2; ++c2) vf1[sl][c2] = vread(VB, 1, sl, c2);
+      }
+      const bf16x4* vf = ks2 == 0 ? vf0[dt] : vf1[dt];
+      const bf16x8 av = __builtin_shufflevector(vf[0], vf[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      o[dt] = mfma(av, pf[ks2], o[dt]);
+      if constexpr (!LAST) {
+#pragma unroll
+        for (int it = sl * 8 / NPV; it < (sl + 1) * 8 / NPV; ++it) {
+          mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(s_nxt[2 * it], s_nxt[2 * it + 1]));
+          asm volatile("" : "+v"(mxl));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    prep_tail(mxl);
-
-    if (last_sub) {
-      j0 = j1;
-      nv0 = nv1;
-      j1 = j2;
-      nv1 = nv2;
+    if constexpr (!LAST) {
+      check_ref(mxl);
+      cur_nv = snv[0];
     }
   };
 
-  using C0 = std::integral_constant<int, 0>;
-  using C1 = std::integral_constant<int, 1>;
-  // Two stages per loop turn so that the LDS stages and the S registers
-  // alternate statically.
+  using FalseT = std::integral_constant<bool, false>;
+  // PERIOD steps per loop turn so that the LDS stages and the S registers
+  // are compile-time indices. The last stage runs the same step: its S[u+1]
+  // is a product of K data already in LDS with every key masked, which
+  // leaves the softmax state unchanged (a separate last step would need
+  // registers the loop does not have).
+  static_assert(PERIOD == 2, "one step per V stage");
   for (int u = 0; u < nst; u += 2) {
-    step(C1{}, C0{}, u, sA, sB);
-    if (u + 1 < nst) step(C0{}, C1{}, u + 1, sB, sA);
+    run_step(std::integral_constant<int, 0>{}, u, FalseT{});
+    if (u + 1 < nst) run_step(std::integral_constant<int, 1>{}, u + 1, FalseT{});
   }
 
   // ---- epilogue: merge the two key halves of each query half. Wave
@@ -644,17 +689,17 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   }
 }
 
-// LDS of a workgroup: the four stages, or the epilogue's hand-over area if
-// that is larger (eight waves at head dim 128).
+// LDS of a workgroup: KR K stages and two V stages, or the epilogue's
+// hand-over area if that is larger.
 template <int D, int NQG>
 constexpr int smem_elems() {
-  constexpr int stages = 4 * 64 * D;
+  constexpr int stages = (k_ring<D, NQG>() + 2) * 64 * D;
   constexpr int handover = 2 * NQG * ((D / 64) * 16 + 2) * 64 * 2;  // floats -> bf16 units
   return stages > handover ? stages : handover;
 }
 
 // Waves per SIMD: two at head_dim 128 (up to 256 VGPRs each), three at
-// head_dim 64 (up to 168; the kernel needs about 160 there).
+// head_dim 64 (up to 168).
 template <int D>
 constexpr int waves_per_simd() { return D == 64 ? 3 : 2; }
 

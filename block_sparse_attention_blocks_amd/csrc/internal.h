@@ -32,6 +32,9 @@ struct AttnParams {
   int32_t n_wg;             // workgroups with work: batch * hq * nq * qparts
   int32_t head_sync;        // 1: all XCDs on one KV head at a time (grid padded per head)
   float scale_log2;         // softmax scale * log2(e)
+  // Bytes from the first K (V) element of a (batch, KV head) to one past its
+  // last one: the range of the copies' buffer resource (below 2^31).
+  uint32_t k_span_bytes, v_span_bytes;
 };
 
 struct PoolParams {
