@@ -5,8 +5,8 @@ kernels behind the C ABI of ``include/bsattn.h``; PyTorch provides device
 memory and the stream. There is no fallback of any kind: if the library is
 missing, importing this package fails, and a failing call raises
 ``BsAttnError`` with the library's own description (vllm-omni PR #8335,
-Purpose: provider failures propagate without dense fallback or K/V
-expansion).
+Purpose: an error of the attention provider reaches the caller; it is never
+answered by running dense attention instead or by repeating K/V heads).
 
 Tensors: q ``[B, q_len, Hq, D]``, k / v ``[B, kv_len, Hkv, D]``, bf16 on the
 GPU, last dimension contiguous. ``layout`` is a mapping with the integer
@@ -23,7 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbsattn.so")
 
 ATTN_OK = 0
-STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "LAUNCH", 5: "DEVICE"}
+STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "LAUNCH", 5: "DEVICE",
+                6: "SELF_TEST"}
 
 
 class BsAttnError(RuntimeError):

@@ -1,9 +1,10 @@
 // Host side of libbsattn: argument validation, workspace layout, launches,
 // error reporting. The C ABI is declared in include/bsattn.h.
 //
-// Contract points taken from the pages: the selector produces per-query-head
-// block indices and counts and the backend executes them; failures
-// propagate with no dense fallback and no K/V expansion; sparse capability is
+// Contract points taken from the pages: the selector lists KV blocks (and
+// their number) for every query head and query block and the backend runs
+// exactly that list; an error reaches the caller and is never answered with
+// dense attention or repeated K/V heads; sparse capability is
 // checked on its own (vllm-omni PR #8335 "[Core] Add shared block-sparse
 // attention adapters with FlashAttention-4", Purpose). A failure names what
 // failed, the library version and the target (in the spirit of the startup
@@ -295,11 +296,14 @@ size_t attn_select_workspace_size(const attn_shape* shape) {
   return ws_layout(shape).total;
 }
 
-attn_status attn_select_blocks(const attn_shape* s, const void* q, const void* k,
-                               int32_t keep_blocks, int32_t* block_idx, int32_t* block_cnt,
-                               int32_t idx_row_stride, void* workspace, size_t workspace_bytes,
-                               hipStream_t stream) {
-  const char* fn = "attn_select_blocks";
+}  // extern "C"
+
+namespace {
+
+attn_status select_impl(const char* fn, const attn_shape* s, const void* q, const void* k,
+                        int32_t keep_blocks, int32_t* block_idx, int32_t* block_cnt,
+                        int32_t idx_row_stride, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   attn_status st = validate_shape(s, fn);
   if (st != ATTN_OK) return st;
   if ((st = validate_ptr(fn, "q", q)) != ATTN_OK) return st;
@@ -372,6 +376,18 @@ attn_status attn_select_blocks(const attn_shape* s, const void* q, const void* k
   e = bsattn::launch_score_topk(sp, s->head_dim, s->batch, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "score launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_select_blocks(const attn_shape* s, const void* q, const void* k,
+                               int32_t keep_blocks, int32_t* block_idx, int32_t* block_cnt,
+                               int32_t idx_row_stride, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return select_impl("attn_select_blocks", s, q, k, keep_blocks, block_idx, block_cnt,
+                     idx_row_stride, workspace, workspace_bytes, stream);
 }
 
 attn_status attn_block_sparse_fwd(const attn_shape* s, const void* q, const void* k, const void* v,

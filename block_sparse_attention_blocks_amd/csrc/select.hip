@@ -5,7 +5,7 @@
 // block-sparse attention adapters with FlashAttention-4" (Purpose): it
 // produces per-query-head KV-block indices and counts, always keeps the
 // protected KV prefix, and query head h works against KV head h / G (native
-// GQA mapping, no K/V expansion). The pages leave the scoring rule open; the
+// GQA mapping, K/V heads never repeated). The pages leave the scoring rule open; the
 // reading implemented here is block-mean pooling of Q and K with the fp32 dot
 // product of the pooled vectors as the block score, top-k by (score
 // descending, index ascending).
@@ -343,7 +343,9 @@ __global__ void __launch_bounds__(64 * NW) score_topk_kernel(const ScoreParams p
   // per score.
   for (int e0 = wave * 64; e0 < nrows * ncp; e0 += 64 * NW) {
     const int e = e0 + lane;
-    uint64_t marked = __builtin_amdgcn_ballot_w64(e < nrows * ncp && keys_lds[e] == kUndecided);
+    // Slots past the row's candidates (c >= ncand) were never written.
+    uint64_t marked = __builtin_amdgcn_ballot_w64(e < nrows * ncp && (e % ncp) < ncand &&
+                                                  keys_lds[e] == kUndecided);
     while (marked != 0) {
       const int ee = e0 + (int)__builtin_ctzll(marked);
       marked &= marked - 1;

@@ -7,9 +7,9 @@
  * selector produces, per query head and query block, a list of KV-block
  * indices and a count; an attention backend then executes exactly that
  * selection. The protected KV prefix, suffix padding and the native
- * MHA/MQA/GQA head mapping are part of the contract (same section). Provider
- * failures propagate: there is no dense fallback and no K/V expansion, under
- * any condition (same section).
+ * MHA/MQA/GQA head mapping are part of the contract (same section). An error
+ * of the provider reaches the caller: it is never answered by dense attention
+ * or by repeating K/V heads, under any condition (same section).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -90,11 +90,14 @@ typedef struct attn_shape {
 int32_t attn_keep_blocks(int32_t n_kv_blocks, int32_t n_protected, int32_t sparsity_pct);
 
 /* Bytes of device workspace attn_select_blocks needs for `shape` (pooled
- * queries and keys and their norms). 0 if the shape is invalid. */
+ * queries and keys and their norms). The caller takes this scratch once, up
+ * front, and passes it to every call, so no call path allocates (mstar PR
+ * #927, Since the review: the attention wrappers share one workspace taken
+ * at build). 0 if the shape is invalid. */
 size_t attn_select_workspace_size(const attn_shape* shape);
 
-/* Block selector (vllm-omni PR #8335, Purpose: per-query-head block indices
- * and counts; protected KV prefixes).
+/* Block selector (vllm-omni PR #8335, Purpose: a list of KV blocks and its
+ * length per query head and query block; protected KV prefixes).
  *
  * For each (batch b, query head h, query block i) with at least one real row:
  *  1. mean-pool the real rows of the query block and the real keys of every KV
@@ -163,10 +166,10 @@ attn_status attn_dense_causal_fwd(const attn_shape* shape, const void* q, const 
 /* ---------------------------------------------------------------------------
  * Step/layer attention strategy: a thin host layer over the calls above that
  * picks dense or selected-sparse attention per (denoising step, layer)
- * (vllm-omni PR #8583, Purpose: dense/sparse switch by step and layer, a
- * uniform dense-to-sparse switch and a mixed-layer policy, warmup across
- * layouts; PR #8644, Purpose: the first twenty iterations dense, then every
- * layer sparse).
+ * (vllm-omni PR #8583, Purpose: dense or sparse chosen per step and layer,
+ * recipes that turn every layer sparse from one step on or only some layers,
+ * and every layout run once before the first timed step; PR #8644, Purpose:
+ * the first twenty iterations dense, then every layer sparse).
  *
  * Steps [0, dense_steps) run every layer dense. From step dense_steps on,
  * layer l runs sparse when bit l of sparse_layers is set, dense otherwise.
@@ -234,7 +237,9 @@ attn_status attn_query_support(const attn_shape* shape);
 attn_status attn_self_test(void);
 
 /* Description of the last failure on the calling thread ("" if none): the
- * entry point, what failed, the library version and target architecture.
+ * entry point, what failed, the library version and target architecture
+ * (mstar PR #927, Since the review: a misconfigured backend fails at start-up
+ * with an error that names the backend, the GPU and the version).
  * The string belongs to the library and stays valid until the next call of
  * an entry point on the same thread. */
 const char* attn_last_error(void);

@@ -9,7 +9,7 @@ What it computes, step by step, in the order of the method:
 * ``keep_blocks``   - blocks kept per query-block row from a target sparsity;
 * ``pool``          - per-block means of Q and K over valid tokens;
 * ``block_scores``  - fp32 block scores (correctly rounded dot products);
-* ``select``        - per-query-head block indices and counts, protected
+* ``select``        - KV-block lists and their lengths per query head, protected
                       prefix always kept, top-k with ties to the lower index;
 * ``attend``        - non-causal softmax attention over the selected blocks,
                       padded keys excluded, GQA head h -> KV head h // G;
@@ -21,7 +21,7 @@ What it computes, step by step, in the order of the method:
 
 Sources (web pages): vllm-omni PR #8335 "[Core] Add shared block-sparse
 attention adapters with FlashAttention-4" (Purpose: selector producing
-per-query-head block indices/counts, protected KV prefixes, suffix padding,
+block lists with their lengths per query head, protected KV prefixes, suffix padding,
 native MHA/MQA/GQA mapping; 75 % target sparsity); diffusers
 ``examples/cosmos3/cosmos_parallel.py`` (``_repeat_kv_heads``: query head i
 pairs with KV group i // repeats; ``build_gen_key_mask``: padded und and gen

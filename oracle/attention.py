@@ -14,7 +14,7 @@ Semantics, each from the pages:
   mapping);
 * the keys of a query row are the valid keys of the blocks listed for its
   (batch, head, query block) (vllm-omni PR #8335, Purpose: the selector's
-  per-query-head block indices/counts are what the backend executes);
+  the block lists and their lengths per query head are what the backend runs);
 * softmax scale defaults to head_dim ** -0.5 (mstar PR #927, automated
   review);
 * padded query rows produce 0 and lse = -inf, as does a row with no valid key;

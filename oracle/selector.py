@@ -91,8 +91,9 @@ def pool(layout: dict, q_bits: np.ndarray, k_bits: np.ndarray):
     KV block) over valid tokens only.
 
     The pages do not spell out how the selector scores blocks (vllm-omni PR
-    #8335, Purpose, says only that it produces per-query-head block indices and
-    counts). Reading taken: block-mean pooling of Q and K. The mean is the
+    #8335, Purpose, says only that it lists KV blocks, with their number, for
+    each query head and query block). Reading taken: block-mean pooling of Q
+    and K. The mean is the
     exact block sum divided once in fp64 and rounded once to fp32.
 
     Returns qp [B,Hq,NQ,D] fp32, kp [B,Hkv,NK,D] fp32, nq [NQ] and nk [NK]

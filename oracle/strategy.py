@@ -3,10 +3,10 @@ layer) call runs, and what that call computes.
 
 Test infrastructure only (see the package docstring).
 
-From the pages: the attention strategy switches between dense and sparse
-attention by denoising step and by layer (vllm-omni PR #8583, Purpose); its
-recipes are a uniform dense-to-sparse switch and a mixed-layer policy (same
-section); the measured Cosmos3 mixed recipe runs 10 dense steps, then 28 of
+From the pages: the attention strategy chooses dense or sparse attention
+per denoising step and per layer (vllm-omni PR #8583, Purpose); its recipes
+either turn every layer sparse from some step on or make only some layers
+sparse (same section); the measured Cosmos3 mixed recipe runs 10 dense steps, then 28 of
 the 36 generation layers sparse (same page, Test Result table); the MiniMax
 H3 recipe keeps the first twenty denoising iterations dense, then runs every
 one of its 50 DiT layers sparse (vllm-omni PR #8644, Purpose).
