@@ -55,7 +55,7 @@ class AttnStrategy(ctypes.Structure):
 
 
 EXPORTS = ("attn_keep_blocks", "attn_select_workspace_size", "attn_select_blocks",
-           "attn_block_sparse_fwd", "attn_dense_fwd", "attn_dense_causal_fwd",
+           "attn_select_blocks_noalloc", "attn_block_sparse_fwd", "attn_dense_fwd", "attn_dense_causal_fwd",
            "attn_strategy_is_sparse", "attn_strategy_workspace_size", "attn_strategy_fwd",
            "attn_strategy_warmup", "attn_query_support", "attn_self_test", "attn_last_error",
            "attn_version")
@@ -75,6 +75,8 @@ def _load():
     lib.attn_select_workspace_size.restype = SZ
     lib.attn_select_blocks.argtypes = [SH, P, P, I32, P, P, I32, P, SZ, P]
     lib.attn_select_blocks.restype = I32
+    lib.attn_select_blocks_noalloc.argtypes = [SH, P, P, I32, P, P, I32, P]
+    lib.attn_select_blocks_noalloc.restype = I32
     lib.attn_block_sparse_fwd.argtypes = [SH, P, P, P, P, P, I32, P, P, P]
     lib.attn_block_sparse_fwd.restype = I32
     lib.attn_dense_fwd.argtypes = [SH, P, P, P, P, P, P]
@@ -270,6 +272,35 @@ def select_blocks(q, k, layout, keep: int, idx_row_stride=None, *, block_idx=Non
     return block_idx, block_cnt
 
 
+# Bytes of the library's own selector scratch (attn_select_blocks_noalloc).
+SELECT_STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def select_blocks_noalloc(q, k, layout, keep: int, idx_row_stride=None, *, block_idx=None,
+                          block_cnt=None, stream=None):
+    """attn_select_blocks_noalloc: the selector with the library's fixed
+    scratch array instead of a caller workspace (nothing is allocated by the
+    library; the outputs are allocated here unless given). Calls that overlap
+    on one device race on that array."""
+    import torch
+    _check_operands(layout, q, k, block_idx=block_idx, block_cnt=block_cnt)
+    shape = make_shape(layout, q=q, k=k)
+    nq, _, _ = num_blocks(layout)
+    stride = max(int(keep if idx_row_stride is None else idx_row_stride), 1)
+    b, hq = int(layout["batch"]), int(layout["num_q_heads"])
+    if block_idx is not None and int(block_idx.shape[-1]) != stride:
+        raise ValueError(f"block_idx rows hold {int(block_idx.shape[-1])} entries, "
+                         f"idx_row_stride is {stride}")
+    if block_idx is None:
+        block_idx = torch.empty((b, hq, nq, stride), dtype=torch.int32, device=q.device)
+    if block_cnt is None:
+        block_cnt = torch.empty((b, hq, nq), dtype=torch.int32, device=q.device)
+    _check(lib.attn_select_blocks_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), int(keep),
+                                          _ptr(block_idx), _ptr(block_cnt), stride,
+                                          _stream_handle(stream)))
+    return block_idx, block_cnt
+
+
 def block_sparse_attention(q, k, v, block_idx, block_cnt, layout, *, out=None, return_lse=False,
                            stream=None):
     """Attention over the selected blocks (attn_block_sparse_fwd)."""
@@ -411,6 +442,6 @@ def pad_segments(q_gen, k_prefix, v_prefix, k_gen, v_gen, block_q: int, block_k:
 
 __all__ = ["BsAttnError", "AttnShape", "AttnStrategy", "EXPORTS", "LIB_PATH", "lib", "version",
            "last_error", "make_shape", "keep_blocks", "num_blocks", "select_workspace_size",
-           "select_blocks", "block_sparse_attention", "dense_attention", "make_strategy",
+           "select_blocks", "select_blocks_noalloc", "SELECT_STATIC_WORKSPACE_BYTES", "block_sparse_attention", "dense_attention", "make_strategy",
            "strategy_is_sparse", "strategy_workspace_size", "strategy_forward",
            "strategy_warmup", "query_support", "self_test", "pad_segments"]

@@ -15,6 +15,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "bsattn.h"
@@ -378,6 +379,33 @@ attn_status select_impl(const char* fn, const attn_shape* s, const void* q, cons
   return ok();
 }
 
+// Scratch of attn_select_blocks_noalloc: one array per device that holds the
+// pooled vectors, for callers that cannot allocate. Host code never uses the
+// array's name as an address: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept here.
+constexpr size_t kStaticWorkspaceBytes = (size_t)ATTN_SELECT_STATIC_WORKSPACE_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kStaticWorkspaceBytes];
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {};
+
+attn_status static_workspace(const char* fn, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+    return fail(ATTN_ERR_DEVICE, fn, "no HIP device available");
+  if (dev >= 64) return fail(ATTN_ERR_DEVICE, fn, "device ordinal %d too large", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(ATTN_ERR_DEVICE, fn, "cannot find the scratch array on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -388,6 +416,26 @@ attn_status attn_select_blocks(const attn_shape* s, const void* q, const void* k
                                hipStream_t stream) {
   return select_impl("attn_select_blocks", s, q, k, keep_blocks, block_idx, block_cnt,
                      idx_row_stride, workspace, workspace_bytes, stream);
+}
+
+attn_status attn_select_blocks_noalloc(const attn_shape* s, const void* q, const void* k,
+                                       int32_t keep_blocks, int32_t* block_idx,
+                                       int32_t* block_cnt, int32_t idx_row_stride,
+                                       hipStream_t stream) {
+  const char* fn = "attn_select_blocks_noalloc";
+  attn_status st = validate_shape(s, fn);
+  if (st != ATTN_OK) return st;
+  const size_t need = ws_layout(s).total;
+  if (need > kStaticWorkspaceBytes)
+    return fail(ATTN_ERR_WORKSPACE, fn,
+                "the shape needs %zu bytes of selector workspace, the library's fixed array holds "
+                "%zu (use attn_select_blocks with a caller workspace)",
+                need, kStaticWorkspaceBytes);
+  if ((st = check_device(fn)) != ATTN_OK) return st;
+  void* ws = nullptr;
+  if ((st = static_workspace(fn, &ws)) != ATTN_OK) return st;
+  return select_impl(fn, s, q, k, keep_blocks, block_idx, block_cnt, idx_row_stride, ws,
+                     kStaticWorkspaceBytes, stream);
 }
 
 attn_status attn_block_sparse_fwd(const attn_shape* s, const void* q, const void* k, const void* v,

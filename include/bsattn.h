@@ -124,6 +124,26 @@ attn_status attn_select_blocks(const attn_shape* shape, const void* q, const voi
                                int32_t idx_row_stride, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Bytes of the selector scratch array the library holds on each device for
+ * attn_select_blocks_noalloc (64 MiB: the 48k-token and 720p workloads need
+ * 28 MB and 45 MB). */
+#define ATTN_SELECT_STATIC_WORKSPACE_BYTES (64u << 20)
+
+/* attn_select_blocks without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (minus the workspace),
+ * same results, bit for bit. The pooled vectors live in a fixed array of
+ * ATTN_SELECT_STATIC_WORKSPACE_BYTES that the library keeps on every device
+ * it runs on until the process ends; the call allocates nothing. Returns
+ * ATTN_ERR_WORKSPACE if attn_select_workspace_size(shape) exceeds the array.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (other streams, other threads) race and must be serialised by
+ * the caller. */
+attn_status attn_select_blocks_noalloc(const attn_shape* shape, const void* q, const void* k,
+                                       int32_t keep_blocks, int32_t* block_idx,
+                                       int32_t* block_cnt, int32_t idx_row_stride,
+                                       hipStream_t stream);
+
 /* Block-sparse attention (vllm-omni PR #8335, Purpose: the backend executes
  * the selection; diffusers cosmos_parallel.py, cosmos3_cp_attention: the
  * generation pathway's non-causal attention over cat(prefix, gen)).
