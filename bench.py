@@ -34,7 +34,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # MI355X dense bf16 (256 CU x 4096 FLOP/clk x 2.4 GHz)
+FP64_PEAK_TFLOPS = 78.6          # MI355X fp64 (vector and matrix)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 ATTN_KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_blocks_amd", "csrc", "attention.hip")
+SELECT_KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_blocks_amd", "csrc", "select.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 WORKLOAD_TEXT = {
@@ -73,19 +76,72 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3,
                     help="distinct input sets rotated over the steps (twostream: always its 36 layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-blocks", type=int, default=756,
-                    help="query blocks per sampled head in the CPU baseline")
-    ap.add_argument("--cpu-sample-heads", type=int, default=3,
-                    help="query heads sampled in the CPU baseline (about 4 s of oracle work each at 48k)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (a known-size kernel "
                          "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
-    with open(ATTN_KERNEL_SRC, "rb") as f:
+def kernel_source_hash(path=ATTN_KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _profile_fields(path):
+    vals = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#") and not line.startswith(" "):
+                    k, v = line.split(":", 1)
+                    vals[k.strip()] = v.strip()
+    return vals
+
+
+def selector_kernels(name, lay, keep):
+    """The two selector kernels, each against its own roof, from the
+    committed rocprofv3 statistics of this workload (average duration of the
+    profiled run's launches) when they were taken on the current selector
+    source: pooling against HBM bandwidth (algorithmic bytes: the real rows
+    of Q and K read once, the pooled vectors and norms written once; the
+    counters' bytes beside them), scoring and top-k against the fp64 matrix
+    peak (2 D FLOP per (query block, candidate block) pair)."""
+    stats = _profile_fields(os.path.join(PROFILES, f"attn_fwd_{name}_kernel_stats.txt"))
+    if stats.get("select_source_sha256_16") != kernel_source_hash(SELECT_KERNEL_SRC):
+        return None
+    try:
+        pool_ms = float(stats["pool_kernel_avg_ms"])
+        score_ms = float(stats["score_topk_kernel_avg_ms"])
+    except (KeyError, ValueError):
+        return None
+    b, hq, hkv, d = lay["batch"], lay["num_q_heads"], lay["num_kv_heads"], lay["head_dim"]
+    nq, nk = lay["q_len"] // lay["block_q"], lay["kv_len"] // lay["block_k"]
+    real_keys = lay["kv_prefix_valid"] + lay["kv_suffix_valid"]
+    read = 2 * d * b * (lay["q_valid"] * hq + real_keys * hkv)
+    written = b * hq * nq * (8 * d + 8) + b * hkv * nk * (4 * d + 8)
+    pool_bytes = read + written
+    real_qblocks = -(-lay["q_valid"] // lay["block_q"])
+    n_cand = -(-lay["kv_suffix_valid"] // lay["block_k"])
+    score_flops = 2.0 * d * b * hq * real_qblocks * n_cand
+    traffic = _profile_fields(os.path.join(PROFILES, f"attn_fwd_{name}_traffic.txt"))
+    counted = None
+    if traffic.get("select_source_sha256_16") == kernel_source_hash(SELECT_KERNEL_SRC):
+        try:
+            counted = float(traffic["pool_hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            counted = None
+    return {
+        "source": "rocprofv3 kernel statistics in profiles/ (same selector source)",
+        "pool_kernel": {"bound": "hbm", "ms": pool_ms, "algorithmic_bytes": pool_bytes,
+                        "achieved": round(pool_bytes / (pool_ms * 1e-3) / 1e9, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(pool_bytes / (pool_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "traffic": counted},
+        "score_topk_kernel": {"bound": "fp64 matrix", "ms": score_ms, "flops": score_flops,
+                              "achieved": round(score_flops / (score_ms * 1e-3) / 1e12, 3),
+                              "peak": FP64_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(score_flops / (score_ms * 1e-3) / 1e12 / FP64_PEAK_TFLOPS, 4)},
+    }
 
 
 def recorded_traffic(name):
@@ -176,19 +232,6 @@ class SclkSampler:
         return max(self.seen) if len(self.seen) >= self.min_samples else None
 
 
-def selector_bytes(lay, keep):
-    """Algorithmic bytes of one selection call: read Q and K once, write the
-    pooled vectors (queries fp64, keys fp32) and their norms, read them back
-    for the scores, write the lists and counts."""
-    b, hq, hkv, d = lay["batch"], lay["num_q_heads"], lay["num_kv_heads"], lay["head_dim"]
-    nq, nk = lay["q_len"] // lay["block_q"], lay["kv_len"] // lay["block_k"]
-    q = b * lay["q_len"] * hq * d * 2
-    k = b * lay["kv_len"] * hkv * d * 2
-    pooled = b * hq * nq * (d * 8 + 8) + b * hkv * nk * (d * 4 + 8)
-    lists = b * hq * nq * (keep + 1) * 4
-    return q + k + 2 * pooled + lists
-
-
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -247,56 +290,87 @@ def cpu_baseline_causal(case):
     }
 
 
-def cpu_baseline(case, keep, n_blocks, n_heads):
-    """The fp64 oracle, untouched, on a bounded sample of the same workload:
-    for each of the first ``n_heads`` query heads, selection over all its
-    query blocks (skipped for a dense layer, ``keep`` None) and attention for
-    its first ``n_blocks`` query blocks. Reported as effective TFLOP/s of the
-    sampled blocks, the selection time pro-rated to them."""
-    import oracle
-    from threadpoolctl import threadpool_info
+def _cpu_oracle_head(args):
+    """One worker of the CPU baseline: the oracle, untouched, for one query
+    head (BLAS limited to one thread): its selection over every query block
+    (skipped for a dense layer, ``keep`` None) and its attention for the
+    first ``n_blocks`` query blocks. Returns the two phases' seconds, the
+    effective FLOPs of the attended blocks (4 bq bk D per listed tile) and
+    their valid-only FLOPs (4 D per real (row, key) pair)."""
+    lay1, q1, k1, v1, keep, n_blocks = args
+    from threadpoolctl import threadpool_limits
 
-    lay = case.layout
-    hq, hkv = lay["num_q_heads"], lay["num_kv_heads"]
-    grp = hq // hkv
-    n_heads = max(1, min(n_heads, hq))
-    nq = lay["q_len"] // lay["block_q"]
-    n_blocks = min(n_blocks, nq)
-    lay1 = dict(lay, num_q_heads=1, num_kv_heads=1)
-    lay_s = dict(lay1, q_len=n_blocks * lay["block_q"],
-                 q_valid=min(lay["q_valid"], n_blocks * lay["block_q"]))
-    t_sel = t_att = flops = 0.0
-    for h in range(n_heads):
-        g = h // grp
-        q1 = np.ascontiguousarray(case.q[:, :, h:h + 1])
-        k1 = np.ascontiguousarray(case.k[:, :, g:g + 1])
-        v1 = np.ascontiguousarray(case.v[:, :, g:g + 1])
+    import oracle
+    bq, bk, d = lay1["block_q"], lay1["block_k"], lay1["head_dim"]
+    with threadpool_limits(1):
         t0 = time.perf_counter()
         if keep is None:
             idx, cnt = oracle.identity_selection(lay1)
         else:
             idx, cnt = oracle.select(lay1, q1, k1, keep)
-        if keep is not None:
-            t_sel += time.perf_counter() - t0
-        idx_s = idx[:, :, :n_blocks]
-        cnt_s = cnt[:, :, :n_blocks]
+        t_sel = time.perf_counter() - t0 if keep is not None else 0.0
+        lay_s = dict(lay1, q_len=n_blocks * bq, q_valid=min(lay1["q_valid"], n_blocks * bq))
+        idx_s, cnt_s = idx[:, :, :n_blocks], cnt[:, :, :n_blocks]
         t0 = time.perf_counter()
         oracle.attend(lay_s, q1[:, :lay_s["q_len"]], k1, v1, idx_s, cnt_s)
-        t_att += time.perf_counter() - t0
-        flops += 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * float(cnt_s.sum())
-    t = t_sel * n_blocks / nq + t_att
-    threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
-    what = "dense (no selection)" if keep is None else f"selection over all {nq} query blocks " \
-        f"({t_sel:.2f} s, pro-rated)"
+        t_att = time.perf_counter() - t0
+    kvalid = oracle.valid_key_mask(lay1).reshape(-1, bk).sum(axis=1)
+    qvalid = oracle.valid_query_mask(lay_s).reshape(-1, bq).sum(axis=1)
+    flops = valid = 0.0
+    for i in range(n_blocks):
+        c = int(cnt_s[0, 0, i])
+        blocks = idx_s[0, 0, i, :c]
+        flops += 4.0 * bq * bk * d * c
+        valid += 4.0 * d * float(qvalid[i]) * float(kvalid[blocks].sum())
+    return t_sel, t_att, flops, valid
+
+
+def cpu_baseline(case, keep, target_flop_per_head=3e11):
+    """The fp64 oracle, untouched, on a bounded sample of the same workload:
+    one worker process per query head (BLAS limited to one thread each), as
+    many heads as the host lets this process run on (at most 16); each
+    selects over all its query blocks (skipped for a dense layer, ``keep``
+    None) and attends for its first query blocks, about 0.3 TFLOP of
+    attention per head. Reported as effective TFLOP/s of the attended
+    blocks, the selection pro-rated to them, over the slowest worker."""
+    import multiprocessing as mp
+
+    lay = case.layout
+    hq, hkv = lay["num_q_heads"], lay["num_kv_heads"]
+    grp = hq // hkv
+    nq = lay["q_len"] // lay["block_q"]
+    per_block = 4.0 * lay["block_q"] * lay["block_k"] * lay["head_dim"] * \
+        (keep if keep is not None else lay["kv_len"] // lay["block_k"])
+    n_blocks = int(max(1, min(nq, target_flop_per_head // per_block)))
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), hq))
+    lay1 = dict(lay, num_q_heads=1, num_kv_heads=1)
+    tasks = [(lay1, np.ascontiguousarray(case.q[:, :, h:h + 1]),
+              np.ascontiguousarray(case.k[:, :, h // grp:h // grp + 1]),
+              np.ascontiguousarray(case.v[:, :, h // grp:h // grp + 1]), keep, n_blocks)
+             for h in range(workers)]
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(workers) as pool:
+        res = pool.map(_cpu_oracle_head, tasks, chunksize=1)
+    wall = time.perf_counter() - t0
+    per_head = [t_sel * n_blocks / nq + t_att for t_sel, t_att, _, _ in res]
+    t = max(per_head)
+    flops = sum(r[2] for r in res)
+    valid = sum(r[3] for r in res)
+    what = "dense (no selection)" if keep is None else \
+        f"selection over all {nq} query blocks (pro-rated)"
     return {
-        "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"{case.name} layer {case.meta.get('layer', 0)}, query heads 0-{n_heads - 1} of "
-                   f"{hq}: {what} + fp64 attention for {n_blocks} query blocks per head "
-                   f"({t_att:.2f} s); effective FLOPs of those blocks"),
-        "seconds": round(t_sel + t_att, 2),
+        "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+        "sample": (f"{case.name} layer {case.meta.get('layer', 0)}, query heads 0-{workers - 1} of "
+                   f"{hq}, one single-threaded worker process each: {what} + fp64 attention for "
+                   f"the first {n_blocks} of {nq} query blocks; effective FLOPs of those blocks "
+                   f"over the slowest worker"),
+        "valid_only_value": valid / t / 1e12,
+        "effective_tflop": round(flops / 1e12, 4),
+        "valid_only_tflop": round(valid / 1e12, 4),
+        "seconds": round(wall, 2),
         "cpu_model": cpu_model(),
-        "select_seconds": round(t_sel, 2),
-        "attend_seconds": round(t_att, 2),
+        "select_seconds_per_head": round(float(np.mean([r[0] for r in res])), 2),
+        "attend_seconds_per_head": round(float(np.mean([r[1] for r in res])), 2),
     }
 
 
@@ -516,11 +590,8 @@ def main():
     n_sel = sum(1 for _, kind in plan[0] if kind == "sparse")
     if n_sel:
         sel_call_ms = float(np.mean(sel_ms)) / n_sel
-        gbs = selector_bytes(lay, keep) / (sel_call_ms * 1e-3) / 1e9
-        result["selector"] = {"bound": "hbm", "ms_per_call": round(sel_call_ms, 4),
-                              "algorithmic_bytes": selector_bytes(lay, keep),
-                              "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                              "frac": round(gbs / 8000.0, 4)}
+        result["selector"] = {"ms_per_call": round(sel_call_ms, 4),
+                              "kernels": selector_kernels(name, lay, keep)}
     if und_only:
         tiles, pairs = causal_tiles(lay)
         result["config"]["causal_tiles_per_head"] = tiles
@@ -530,8 +601,7 @@ def main():
             result["cpu_baseline"] = cpu_baseline_causal(case0)
         else:
             cb_case = sparse_case if sparse_case is not None else case0
-            result["cpu_baseline"] = cpu_baseline(cb_case, keep if sparse_case is not None else None,
-                                                  args.cpu_sample_blocks, args.cpu_sample_heads)
+            result["cpu_baseline"] = cpu_baseline(cb_case, keep if sparse_case is not None else None)
     print(json.dumps(result), flush=True)
 
 

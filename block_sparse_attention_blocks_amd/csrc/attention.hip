@@ -48,10 +48,11 @@
 //    VGPR staging): the buffer resource of the (batch, KV head) and each
 //    lane's offset are fixed, the stage enters as one scalar byte offset.
 //    Rows are XOR-swizzled in 16-byte chunks so the K row reads and the V
-//    transpose reads hit distinct banks. K is copied KR - 1 stages ahead of
-//    its use (a ring of KR stages), V one stage ahead (two stages), so a
-//    stage's wait leaves the newest K copies in flight. One workgroup
-//    barrier per stage.
+//    transpose reads hit distinct banks. K and V each have a ring of R
+//    stages in LDS and are copied R - 1 stages ahead of their use, so a
+//    stage's wait leaves the copies of the R - 2 newest stages in flight:
+//    a copy has R - 1 stages of time to land. One workgroup barrier per
+//    stage.
 //  * The block list is read 64 entries per vector load; each entry becomes a
 //    descriptor (first key row, real keys in the block) once, and a stage
 //    takes its descriptor with one v_readlane.
@@ -128,11 +129,15 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// K stages in LDS. Two (K copied one stage ahead, like V) keep the main loop
-// within 256 registers; a ring of three needs the loop unrolled six stages
-// deep, and the longer live ranges then spill the Q fragments.
+// Stages of K (and of V) in LDS: two of each. A 64-row workgroup shares its
+// CU with another one and has 64 KB of LDS. A 128-row workgroup has the
+// CU's LDS to itself and could hold four stages of each, but copying three
+// stages ahead measured 3-9 % slower than one (on gfx950 these copies cost
+// through the power they draw, not through their latency). The loop is
+// unrolled R stages deep (a ring of three would need six, and the longer
+// live ranges then spill the Q fragments).
 template <int D, int NQG>
-constexpr int k_ring() { return 2; }
+constexpr int kv_ring() { return 2; }
 
 template <int D, int BK, int NQG, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ smem) {
@@ -149,8 +154,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   constexpr int RPI = 64 / CPR;  // rows moved by one copy instruction (64 lanes x 16 bytes)
   constexpr int NL = RPW / RPI;  // copy instructions per wave for one K (or V) stage
   static_assert(NL >= 1 && NL * RPI == RPW, "rows per wave");
-  constexpr int KR = k_ring<D, NQG>();    // K stages in LDS (K is copied KR - 1 stages ahead)
-  constexpr int PERIOD = KR % 2 ? 2 * KR : KR;  // steps after which every buffer index repeats
+  constexpr int R = kv_ring<D, NQG>();   // K and V stages in LDS (copied R - 1 stages ahead)
+  static_assert(R == 2 || R == 4, "rings of two or four stages");
   // A row moves its reference max only when a stage max exceeds it by more
   // than this many powers of two; until then probabilities are taken against
   // the stale max and stay below 2^8, far from fp32 or bf16 overflow.
@@ -311,7 +316,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   }
   lds_u16* const lds = (lds_u16*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
-  // LDS: K stages 0 .. KR - 1, then V stages 0, 1. A copy instruction writes
+  // LDS: K stages 0 .. R - 1, then V stages 0 .. R - 1. A copy instruction writes
   // 64 lanes x 16 bytes from M0 on, rows RPW wave + RPI it .. of its stage.
   // The copies are issued from inline assembly: the compiler then neither
   // counts them nor orders LDS reads behind them (it cannot tell that they
@@ -330,7 +335,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   };
   auto copy_v = [&](auto vb_c, int it, int row) {
     constexpr int VB = decltype(vb_c)::value;
-    copy_one(vrsrc, lds_addr + (uint32_t)(((KR + VB) * STAGE + (wave * RPW + it * RPI) * D) * 2),
+    copy_one(vrsrc, lds_addr + (uint32_t)(((R + VB) * STAGE + (wave * RPW + it * RPI) * D) * 2),
              vvoff[it], row * vrow_b);
   };
 
@@ -360,7 +365,7 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       const int d = dt * 32 + 16 * (g16 & 1) + 4 * q4;
       const int row = 8 * c2 + 4 * half + tq;  // + 32 kh + 16 per key step
       vrd[dt][c2] =
-          (KR * STAGE + (32 * kh + row) * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7)) * 2;
+          (R * STAGE + (32 * kh + row) * D + (((d >> 3) ^ swz<CPR>(row)) << 3) + (d & 7)) * 2;
       asm volatile("" : "+v"(vrd[dt][c2]));
     }
   typedef __attribute__((address_space(3))) char lds_char;
@@ -439,33 +444,45 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   };
 
   // Descriptors of the stages in the pipeline: before step u, index x holds
-  // stage u + x (x < KR); the step shifts them, so that index x then holds
-  // stage u + 1 + x and the new stage u + KR enters at index KR - 1.
-  int srow[KR], snv[KR];
+  // stage u + x (x < R); the step shifts them, so that index x then holds
+  // stage u + 1 + x and the new stage u + R enters at index R - 1.
+  int srow[R], snv[R];
 #pragma unroll
-  for (int x = 0; x < KR; ++x) srow[x] = snv[x] = 0;
+  for (int x = 0; x < R; ++x) srow[x] = snv[x] = 0;
   f32x16 sbuf[2];
 
+  // Outstanding copies a step's wait leaves in flight: those of the R - 2
+  // newest steps (V, then K, NL instructions each).
+  constexpr int INFLIGHT = (R - 2) * 2 * NL;
   if (nst > 0) {
-    // Prologue: K of stages 0 .. KR - 1 and V of stage 0, then S[0].
+    // Prologue: K of stages 0 .. R - 1 and V of stages 0 .. R - 2, in the
+    // order K0 V0 K1 V1 ..., then S[0] once K0 has landed.
     stage_desc(std::integral_constant<int, 0>{}, 0, srow[0], snv[0]);
 #pragma unroll
-    for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, 0>{}, it, srow[0]);
-#pragma unroll
-    for (int it = 0; it < NL; ++it) copy_v(std::integral_constant<int, 0>{}, it, srow[0]);
-    srow[1] = srow[0];
-    snv[1] = snv[0];
-    stage_desc(std::integral_constant<int, 1 % SPB>{}, 1, srow[1], snv[1]);
-#pragma unroll
-    for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, 1>{}, it, srow[1]);
-    if constexpr (KR == 3) {
-      srow[2] = srow[1];
-      snv[2] = snv[1];
-      stage_desc(std::integral_constant<int, 2 % SPB>{}, 2, srow[2], snv[2]);
-#pragma unroll
-      for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, 2>{}, it, srow[2]);
+    for (int x = 1; x < R; ++x) {
+      srow[x] = srow[x - 1];
+      snv[x] = snv[x - 1];
+      if (x % SPB == 0)
+        stage_desc(std::integral_constant<int, 0>{}, x, srow[x], snv[x]);
+      else
+        stage_desc(std::integral_constant<int, 1 % SPB>{}, x, srow[x], snv[x]);
     }
-    wait_vmcnt<0>();
+    auto pro_copies = [&](auto x_c) {
+      constexpr int X = decltype(x_c)::value;
+#pragma unroll
+      for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, X>{}, it, srow[X]);
+      if constexpr (X + 1 < R) {
+#pragma unroll
+        for (int it = 0; it < NL; ++it) copy_v(std::integral_constant<int, X>{}, it, srow[X]);
+      }
+    };
+    pro_copies(std::integral_constant<int, 0>{});
+    pro_copies(std::integral_constant<int, 1>{});
+    if constexpr (R == 4) {
+      pro_copies(std::integral_constant<int, 2 % R>{});
+      pro_copies(std::integral_constant<int, 3 % R>{});
+    }
+    wait_vmcnt<(2 * R - 2) * NL>();  // K of stage 0
     lds_barrier();
 #pragma unroll
     for (int r = 0; r < 16; ++r) sbuf[0][r] = 0.0f;
@@ -477,43 +494,34 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     mask(sbuf[0], snv[0], srow[0]);
     check_ref(row_max(sbuf[0]));
   }
-  static_assert(KR == 2 || KR == 3, "K ring of two or three stages");
 
-  // One pipeline step on stage u (step S of the period, u % PERIOD == S).
-  // K stage u + 1 is read from K buffer (S + 1) % KR, V stage u from V buffer
-  // S % 2; the step copies V of u + 1 into V buffer (S + 1) % 2 and K of
-  // u + KR into K buffer S % KR. Both were last read in the previous step,
-  // which every wave has left at the barrier. LAST: stage u is the last one
-  // (no S[u+1] and no copies).
+  // One pipeline step on stage u (step S of the unrolled loop, u % R == S).
+  // K stage u + 1 is read from K buffer (S + 1) % R and V stage u from V
+  // buffer S; the step copies K of u + R into K buffer S (last read for
+  // S[u], in the previous step) and V of u + R - 1 into V buffer
+  // (S + R - 1) % R (last read for PV of u - 1, in the previous step):
+  // every wave has left the previous step at this step's barrier.
   int cur_nv = snv[0];  // real keys of the current stage
-  auto run_step = [&](auto s_c, int u, auto last_c) {
+  auto run_step = [&](auto s_c, int u) {
     constexpr int S = decltype(s_c)::value;
-    constexpr bool LAST = decltype(last_c)::value;
-    constexpr int KB = (S + 1) % KR, VB = S % 2;
-    constexpr int KNEW = S % KR, VNEW = (S + 1) % 2;
+    constexpr int KB = (S + 1) % R, VB = S;
+    constexpr int KNEW = S, VNEW = (S + R - 1) % R;
     f32x16& s_cur = sbuf[S % 2];
     f32x16& s_nxt = sbuf[(S + 1) % 2];
-    if constexpr (!LAST) {
-      // Index x now holds stage u + 1 + x; stage u + KR enters at KR - 1.
+    // Index x now holds stage u + 1 + x; stage u + R enters at R - 1.
 #pragma unroll
-      for (int x = 0; x + 1 < KR; ++x) {
-        srow[x] = srow[x + 1];
-        snv[x] = snv[x + 1];
-      }
-      stage_desc(std::integral_constant<int, (S + KR) % SPB>{}, u + KR, srow[KR - 1],
-                 snv[KR - 1]);
+    for (int x = 0; x + 1 < R; ++x) {
+      srow[x] = srow[x + 1];
+      snv[x] = snv[x + 1];
     }
+    stage_desc(std::integral_constant<int, (S + R) % SPB>{}, u + R, srow[R - 1], snv[R - 1]);
     // ---- the step's single synchronisation point: V of u and K of u + 1
-    // have landed; with a ring of three K stages the copies of K of u + 2
-    // (issued last) may still be in flight.
-    if constexpr (LAST || KR == 2) {
-      wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<NL>();
-    }
+    // have landed (this wave's copies by the count, every wave's by the
+    // barrier).
+    wait_vmcnt<INFLIGHT>();
     lds_barrier();
     const uint16_t* kb = smem + KB * STAGE;
-    uint16_t* vb = smem + (KR + VB) * STAGE;
+    uint16_t* vb = smem + (R + VB) * STAGE;
     {
       const int nvs = min(max(cur_nv - 32 * kh, 0), 32);
       if (nvs < 32) {
@@ -540,26 +548,22 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     constexpr int CEVERY = KS / NCOPY;
     bf16x8 kf[3];
     float lsa = 0.0f, lsb = 0.0f;  // row sum of the stage's probabilities (fp32)
-    if constexpr (!LAST) {
-      kf[0] = *reinterpret_cast<const bf16x8*>(kb + koffs[0]);
-      kf[1] = *reinterpret_cast<const bf16x8*>(kb + koffs[1]);
+    kf[0] = *reinterpret_cast<const bf16x8*>(kb + koffs[0]);
+    kf[1] = *reinterpret_cast<const bf16x8*>(kb + koffs[1]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
-    }
+    for (int r = 0; r < 16; ++r) s_nxt[r] = 0.0f;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-      if constexpr (!LAST) {
-        if (k + 2 < KS) kf[(k + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + koffs[k + 2]);
-        s_nxt = mfma(kf[k % 3], qf[k], s_nxt);
-        // The copy instructions spread evenly over the slots (V of u + 1,
-        // then K of u + KR).
-        if (k % CEVERY == 0) {
-          const int c = k / CEVERY;
-          if (c < NL) {
-            copy_v(std::integral_constant<int, VNEW>{}, c, srow[0]);
-          } else {
-            copy_k(std::integral_constant<int, KNEW>{}, c - NL, srow[KR - 1]);
-          }
+      if (k + 2 < KS) kf[(k + 2) % 3] = *reinterpret_cast<const bf16x8*>(kb + koffs[k + 2]);
+      s_nxt = mfma(kf[k % 3], qf[k], s_nxt);
+      // The copy instructions spread evenly over the slots (V of u + R - 1,
+      // then K of u + R).
+      if (k % CEVERY == 0) {
+        const int c = k / CEVERY;
+        if (c < NL) {
+          copy_v(std::integral_constant<int, VNEW>{}, c, srow[R - 2]);
+        } else {
+          copy_k(std::integral_constant<int, KNEW>{}, c - NL, srow[R - 1]);
         }
       }
 #pragma unroll
@@ -585,7 +589,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     }
     lsum += lsa + lsb;
 
-    if constexpr (!LAST) mask(s_nxt, u + 1 < nst ? snv[0] : 0, srow[0]);
+    // With no stage u + 1 (past the end of the list) S[u+1] is a product of
+    // K data already in LDS with every key masked: the softmax state stays.
+    mask(s_nxt, u + 1 < nst ? snv[0] : 0, srow[0]);
     // ---- (b) O += V^T P[u]^T || row max of S[u+1].
     float mxl = -__builtin_inff();
     constexpr int NPV = 2 * DT;
@@ -599,31 +605,32 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       const bf16x4* vf = ks2 == 0 ? vf0[dt] : vf1[dt];
       const bf16x8 av = __builtin_shufflevector(vf[0], vf[1], 0, 1, 2, 3, 4, 5, 6, 7);
       o[dt] = mfma(av, pf[ks2], o[dt]);
-      if constexpr (!LAST) {
 #pragma unroll
-        for (int it = sl * 8 / NPV; it < (sl + 1) * 8 / NPV; ++it) {
-          mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(s_nxt[2 * it], s_nxt[2 * it + 1]));
-          asm volatile("" : "+v"(mxl));
-        }
+      for (int it = sl * 8 / NPV; it < (sl + 1) * 8 / NPV; ++it) {
+        mxl = __builtin_fmaxf(mxl, __builtin_fmaxf(s_nxt[2 * it], s_nxt[2 * it + 1]));
+        asm volatile("" : "+v"(mxl));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!LAST) {
-      check_ref(mxl);
-      cur_nv = snv[0];
-    }
+    check_ref(mxl);
+    cur_nv = snv[0];
   };
 
-  using FalseT = std::integral_constant<bool, false>;
-  // PERIOD steps per loop turn so that the LDS stages and the S registers
-  // are compile-time indices. The last stage runs the same step: its S[u+1]
-  // is a product of K data already in LDS with every key masked, which
-  // leaves the softmax state unchanged (a separate last step would need
-  // registers the loop does not have).
-  static_assert(PERIOD == 2, "one step per V stage");
-  for (int u = 0; u < nst; u += 2) {
-    run_step(std::integral_constant<int, 0>{}, u, FalseT{});
-    if (u + 1 < nst) run_step(std::integral_constant<int, 1>{}, u + 1, FalseT{});
+  // R steps per loop turn so that the LDS stages and the S registers are
+  // compile-time indices. The last stage runs the same step: its S[u+1] is
+  // a product of K data already in LDS with every key masked, which leaves
+  // the softmax state unchanged (a separate last step would need registers
+  // the loop does not have); its copies read the last stage's rows again.
+  for (int u = 0; u < nst; u += R) {
+    run_step(std::integral_constant<int, 0>{}, u);
+    if (u + 1 >= nst) break;
+    run_step(std::integral_constant<int, 1>{}, u + 1);
+    if constexpr (R == 4) {
+      if (u + 2 >= nst) break;
+      run_step(std::integral_constant<int, 2 % R>{}, u + 2);
+      if (u + 3 >= nst) break;
+      run_step(std::integral_constant<int, 3 % R>{}, u + 3);
+    }
   }
 
   // ---- epilogue: merge the two key halves of each query half. Wave
@@ -689,11 +696,11 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   }
 }
 
-// LDS of a workgroup: KR K stages and two V stages, or the epilogue's
+// LDS of a workgroup: R K stages and R V stages, or the epilogue's
 // hand-over area if that is larger.
 template <int D, int NQG>
 constexpr int smem_elems() {
-  constexpr int stages = (k_ring<D, NQG>() + 2) * 64 * D;
+  constexpr int stages = 2 * kv_ring<D, NQG>() * 64 * D;
   constexpr int handover = 2 * NQG * ((D / 64) * 16 + 2) * 64 * 2;  // floats -> bf16 units
   return stages > handover ? stages : handover;
 }
