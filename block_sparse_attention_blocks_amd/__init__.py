@@ -20,7 +20,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsattn.so")
+# Which build of the library to load: the release build next to this file
+# unless BSATTN_LIBRARY names another (the tests use it for the list-checking
+# and host-sanitized builds).
+LIB_PATH = os.environ.get("BSATTN_LIBRARY") or os.path.join(_HERE, "libbsattn.so")
 
 ATTN_OK = 0
 STATUS_NAMES = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "WORKSPACE", 4: "LAUNCH", 5: "DEVICE",

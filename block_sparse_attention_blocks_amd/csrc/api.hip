@@ -20,6 +20,13 @@
 
 #include "bsattn.h"
 #include "internal.h"
+#include "listcheck.h"
+
+// Builds compiled with BSATTN_CHECK_LISTS=1 (libbsattn_checked.so) validate
+// every real query block's list on the device before block-sparse attention.
+#ifndef BSATTN_CHECK_LISTS
+#define BSATTN_CHECK_LISTS 0
+#endif
 
 #define BSATTN_VERSION "0.1.0"
 #define BSATTN_TARGET "gfx950"
@@ -214,6 +221,77 @@ float scale_of(const attn_shape* s) {
   return s->softmax_scale > 0.0f ? s->softmax_scale : 1.0f / std::sqrt((float)s->head_dim);
 }
 
+#if BSATTN_CHECK_LISTS
+// The first faulty list, as ((row << 32) | ((slot + 1) << 2) | fault): the
+// smallest row wins, so the report does not depend on the schedule.
+__device__ unsigned long long g_list_fault;
+
+constexpr int kCheckRows = 64;         // rows per workgroup, one per thread
+constexpr int kCheckMaxBlocks = 4096;  // KV blocks a thread's LDS bitmap covers
+
+__global__ void __launch_bounds__(kCheckRows)
+check_lists_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+                   int32_t stride, int32_t nk, int32_t nq, int32_t real_qblocks, int64_t rows) {
+  __shared__ uint32_t seen[kCheckRows][kCheckMaxBlocks / 32];
+  const int64_t row = (int64_t)blockIdx.x * kCheckRows + threadIdx.x;
+  if (row >= rows || (int32_t)(row % nq) >= real_qblocks) return;
+  int32_t pos = -1;
+  const int32_t f =
+      bsattn::check_list_row(idx + row * stride, cnt[row], stride, nk,
+                             nk <= kCheckMaxBlocks ? seen[threadIdx.x] : nullptr, &pos);
+  if (f != bsattn::kListOk) {
+    const unsigned long long key = ((unsigned long long)row << 32) |
+                                   ((unsigned long long)(uint32_t)(pos + 1) << 2) |
+                                   (unsigned long long)f;
+    atomicMin(&g_list_fault, key);
+  }
+}
+
+// Runs the list check on `stream` and waits for it. Rows of query blocks with
+// no real query row are not read by the attention kernel and not checked.
+attn_status check_lists(const char* fn, const attn_shape* s, const Derived& d, const int32_t* idx,
+                        const int32_t* cnt, int32_t stride, hipStream_t stream) {
+  const int64_t rows = (int64_t)s->batch * s->num_q_heads * d.nq;
+  const int32_t real_qblocks = (int32_t)ceil_div(s->q_valid, s->block_q);
+  const unsigned long long none = ~0ull;
+  unsigned long long got = none;
+  hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_list_fault), &none, sizeof none, 0,
+                                        hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) {
+    const int64_t grid = (rows + kCheckRows - 1) / kCheckRows;
+    hipLaunchKernelGGL(check_lists_kernel, dim3((unsigned)grid), dim3(kCheckRows), 0, stream, idx,
+                       cnt, stride, d.nk, d.nq, real_qblocks, rows);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbolAsync(&got, HIP_SYMBOL(g_list_fault), sizeof got, 0,
+                                 hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "list check failed: %s", hipGetErrorString(e));
+  if (got == none) return ATTN_OK;
+  const int64_t row = (int64_t)(got >> 32);
+  const int32_t slot = (int32_t)((got >> 2) & 0x3FFFFFFFu) - 1;
+  const int32_t fault = (int32_t)(got & 3u);
+  const int32_t i = (int32_t)(row % d.nq);
+  const int32_t h = (int32_t)((row / d.nq) % s->num_q_heads);
+  const int32_t b = (int32_t)(row / d.nq / s->num_q_heads);
+  int32_t count = 0, entry = 0;
+  (void)hipMemcpy(&count, cnt + row, sizeof count, hipMemcpyDeviceToHost);
+  if (slot >= 0) (void)hipMemcpy(&entry, idx + row * stride + slot, sizeof entry, hipMemcpyDeviceToHost);
+  if (fault == bsattn::kListCount)
+    return fail(ATTN_ERR_INVALID_ARG, fn,
+                "block list of (batch %d, head %d, query block %d): count %d outside [0, %d]", b, h,
+                i, count, stride);
+  if (fault == bsattn::kListRange)
+    return fail(ATTN_ERR_INVALID_ARG, fn,
+                "block list of (batch %d, head %d, query block %d): entry %d is %d, outside [0, %d)",
+                b, h, i, slot, entry, d.nk);
+  return fail(ATTN_ERR_INVALID_ARG, fn,
+              "block list of (batch %d, head %d, query block %d): entry %d repeats block %d", b, h,
+              i, slot, entry);
+}
+#endif
+
 attn_status run_attention(const char* fn, const attn_shape* s, const void* q, const void* k,
                           const void* v, const int32_t* idx, const int32_t* cnt,
                           int32_t idx_row_stride, void* out, float* lse, int mode,
@@ -273,6 +351,12 @@ attn_status run_attention(const char* fn, const attn_shape* s, const void* q, co
   if (p.n_wg == 0) return ok();
   st = check_device(fn);
   if (st != ATTN_OK) return st;
+#if BSATTN_CHECK_LISTS
+  if (!dense) {
+    st = check_lists(fn, s, d, idx, cnt, idx_row_stride, stream);
+    if (st != ATTN_OK) return st;
+  }
+#endif
   const hipError_t e = bsattn::launch_attention(p, s->head_dim, s->block_q, s->block_k, mode, stream);
   if (e != hipSuccess) return fail(ATTN_ERR_LAUNCH, fn, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

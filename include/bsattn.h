@@ -154,8 +154,14 @@ attn_status attn_select_blocks_noalloc(const attn_shape* shape, const void* q, c
  * h / (Hq/Hkv), cnt = block_cnt[b,h,i] clamped to [0, idx_row_stride].
  * bf16 inputs, fp32 accumulation and softmax, bf16 output. Rows with no key
  * (cnt 0, or only padded keys) and padded rows give 0 and lse -inf. Listed
- * blocks should be distinct and in [0, NK); entries outside that range are
- * skipped, the order of the list does not matter. */
+ * blocks should be distinct and in [0, NK); the order of the list does not
+ * matter. The release build skips entries outside [0, NK) and counts a
+ * repeated block twice. The list-checking build (libbsattn_checked.so,
+ * compiled with BSATTN_CHECK_LISTS=1) first checks the list of every query
+ * block that has a real row, on `stream`, and waits for the check: a count
+ * outside [0, idx_row_stride], an entry outside [0, NK) or a repeated entry
+ * returns ATTN_ERR_INVALID_ARG naming the lowest such (batch, head, query
+ * block), and nothing is written. */
 attn_status attn_block_sparse_fwd(const attn_shape* shape, const void* q, const void* k,
                                   const void* v, const int32_t* block_idx,
                                   const int32_t* block_cnt, int32_t idx_row_stride, void* out,

@@ -142,10 +142,12 @@ def test_selector_block_limit():
     assert st == 2 and "4096" in msg
 
 
-def test_binding_fails_loudly_without_library(tmp_path):
-    """Importing the binding with the library absent raises (no CPU fallback)."""
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    """Importing the binding with the library absent raises (no CPU fallback),
+    also when BSATTN_LIBRARY names a file that does not exist."""
     import importlib.util
     import shutil
+    monkeypatch.delenv("BSATTN_LIBRARY", raising=False)
     pkg = os.path.join(ROOT, "block_sparse_attention_blocks_amd")
     dst = tmp_path / "block_sparse_attention_blocks_amd"
     dst.mkdir()
@@ -154,6 +156,11 @@ def test_binding_fails_loudly_without_library(tmp_path):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+    monkeypatch.setenv("BSATTN_LIBRARY", str(tmp_path / "absent" / "libbsattn.so"))
+    mod2 = importlib.util.module_from_spec(
+        importlib.util.spec_from_file_location("bsa_nolib2", os.path.join(pkg, "__init__.py")))
+    with pytest.raises(ImportError):
+        mod2.__spec__.loader.exec_module(mod2)
 
 
 def _golden_recipes():
