@@ -57,8 +57,8 @@
 //    descriptor (first key row, real keys in the block) once, and a stage
 //    takes its descriptor with one v_readlane.
 //  * Workgroups are renumbered so that each XCD works through a contiguous
-//    range of (KV head, query block), keeping that range's K/V tiles in the
-//    XCD's L2.
+//    range of (KV head, query head, query block), keeping that range's K/V
+//    tiles in the XCD's L2.
 
 #include <type_traits>
 #include <utility>
@@ -168,12 +168,14 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // Workgroup w runs on XCD w % 8. The work is the (batch, KV head, query
-  // block, head-in-group, part) order; a query block of more than 128 rows
-  // is split into parts of 32 NQG rows, one workgroup each, reading the same
-  // list. Each XCD takes a contiguous range of that order, so neighbours
-  // (the heads of a group, adjacent query blocks: similar lists) share its
-  // L2. When the K/V of all heads would not fit in the 256 MB last-level
+  // Workgroup w runs on XCD w % 8. The work is the (batch, KV head,
+  // head-in-group, query block, part) order; a query block of more than 128
+  // rows is split into parts of 32 NQG rows, one workgroup each, reading the
+  // same list. Each XCD takes a contiguous range of that order, so the
+  // workgroups it runs together are adjacent query blocks of one query head,
+  // whose lists are the most alike (on the 48k inputs adjacent blocks of a
+  // head share 61 % of their lists, the heads of a group 34 %), and read
+  // many of the same K/V blocks through its L2. When the K/V of all heads would not fit in the 256 MB last-level
   // cache together, the XCDs instead split every (batch, KV head) eight ways
   // and move through the KV heads in step, so only one head's K/V is live;
   // the grid is then padded to a multiple of eight per (batch, KV head).
@@ -195,8 +197,8 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   }
   const int part = lin % p.qparts;
   int t = lin / p.qparts;
-  const int hig = t % p.group;
-  const int i = t / p.group;
+  const int hig = t / p.nq;
+  const int i = t % p.nq;
   const int g = bg % p.hkv;
   const int b = bg / p.hkv;
   const int h = g * p.group + hig;
