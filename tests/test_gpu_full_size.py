@@ -74,6 +74,20 @@ def _select_and_compare(case, keep):
     return (q, k, v, idx, cnt, stream), (ridx, rcnt)
 
 
+def _run_again_bitwise(case, keep, q, k, v, idx, cnt, out, lse, stream):
+    """A second selection and attention call on the same inputs must give the
+    same bytes: the workgroup order (XCD remap, dispatch cohorts, the
+    head-synchronous order at 720p) depends on blockIdx only."""
+    lay = case.layout
+    idx2, cnt2 = bsa.select_blocks(q, k, lay, keep, keep, stream=stream)
+    out2, lse2 = bsa.block_sparse_attention(q, k, v, idx2, cnt2, lay, return_lse=True,
+                                            stream=stream)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(cnt2, cnt), "second selection differs"
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16)), "second output differs"
+    assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32)), "second lse differs"
+
+
 def _check_every_row(case, out, lse, idx, cnt, what):
     mx, mean, lse_err, pad_zero, lse_fin = check_every_row(
         case, np.asarray(idx), np.asarray(cnt), out.view(torch.int16).cpu().numpy().view(np.uint16),
@@ -98,6 +112,7 @@ def test_edge48k_bench_launch():
     out, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, out=out, return_lse=True,
                                           stream=stream)
     torch.cuda.synchronize()
+    _run_again_bitwise(case, keep, q, k, v, idx, cnt, out, lse, stream)
     _check_every_row(case, out, lse, ridx, rcnt, "sparse")
 
 
@@ -152,6 +167,7 @@ def test_video720p_full_size():
     (q, k, v, idx, cnt, stream), (ridx, rcnt) = _select_and_compare(case, keep)
     out, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, return_lse=True, stream=stream)
     torch.cuda.synchronize()
+    _run_again_bitwise(case, keep, q, k, v, idx, cnt, out, lse, stream)
     _check_rows(case, out, lse, ridx, rcnt, 256, what="sparse")
 
 
