@@ -132,8 +132,10 @@ attn_status validate_shape(const attn_shape* s, const char* fn) {
   // 32-bit byte offsets and packs a block's first key row into 23 bits.
   if (s->kv_len > (1 << 23))
     return fail(ATTN_ERR_UNSUPPORTED, fn, "kv_len %d > %d", s->kv_len, 1 << 23);
-  if (kv_span_bytes(s->kv_len, s->k_stride[1], s->head_dim) > 0x7FFFFFFF ||
-      kv_span_bytes(s->kv_len, s->v_stride[1], s->head_dim) > 0x7FFFFFFF)
+  // The attention kernel addresses one KV head's rows through a buffer
+  // resource of 31-bit range that starts up to 3 KB before them.
+  if (kv_span_bytes(s->kv_len, s->k_stride[1], s->head_dim) > 0x7FFFFFFF - 4096 ||
+      kv_span_bytes(s->kv_len, s->v_stride[1], s->head_dim) > 0x7FFFFFFF - 4096)
     return fail(ATTN_ERR_UNSUPPORTED, fn,
                 "one KV head spans more than 2 GiB (kv_len %d, k row stride %lld, v row stride %lld)",
                 s->kv_len, (long long)s->k_stride[1], (long long)s->v_stride[1]);

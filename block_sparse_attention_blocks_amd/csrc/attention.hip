@@ -301,44 +301,78 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   // Copies: one buffer resource per (batch, KV head) for K and for V, a fixed
   // per-lane byte offset per copy instruction (row within the stage and
   // swizzled chunk), and the stage's first key row as a scalar byte offset.
-  const uint16_t* kbase = p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2;
-  const uint16_t* vbase = p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2;
-  const auto krsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), 0,
-                                                       p.k_span_bytes, 0x00020000);
-  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), 0,
-                                                       p.v_span_bytes, 0x00020000);
+  // Copy instruction `it` of a stage writes LDS 1 KB further on than copy
+  // it - 1; that step is the instruction's immediate offset, which moves the
+  // LDS and the memory address alike, so it is taken back out of the lane's
+  // memory offset and M0 is set once per stage buffer. The resources start
+  // (NL - 1) KB before the head's first row (and reach as much further), so
+  // that the lane offsets stay non-negative for any row stride; every address
+  // a copy reads is still inside the head's rows.
+  static_assert(NL <= 4, "copy offsets fit the 12-bit immediate");
+  constexpr uint32_t SHIFT = (NL - 1) * 1024;
+  const uintptr_t kbase = (uintptr_t)(p.k + (int64_t)b * p.ks0 + (int64_t)g * p.ks2);
+  const uintptr_t vbase = (uintptr_t)(p.v + (int64_t)b * p.vs0 + (int64_t)g * p.vs2);
+  const auto krsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase - SHIFT), 0,
+                                                       p.k_span_bytes + SHIFT, 0x00020000);
+  const auto vrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase - SHIFT), 0,
+                                                       p.v_span_bytes + SHIFT, 0x00020000);
   const int krow_b = (int)p.ks1 * 2, vrow_b = (int)p.vs1 * 2;  // bytes per key row
   int kvoff[NL], vvoff[NL];
 #pragma unroll
   for (int it = 0; it < NL; ++it) {
     const int row = wave * RPW + it * RPI + lane / CPR;  // row within the stage
     const int gch = (lane % CPR) ^ swz<CPR>(row);         // chunk this lane's LDS slot holds
-    kvoff[it] = row * krow_b + gch * 16;
-    vvoff[it] = row * vrow_b + gch * 16;
+    kvoff[it] = row * krow_b + gch * 16 + (int)SHIFT - it * 1024;
+    vvoff[it] = row * vrow_b + gch * 16 + (int)SHIFT - it * 1024;
   }
   lds_u16* const lds = (lds_u16*)smem;
   const uint32_t lds_addr = (uint32_t)(uintptr_t)lds;
   // LDS: K stages 0 .. R - 1, then V stages 0 .. R - 1. A copy instruction writes
-  // 64 lanes x 16 bytes from M0 on, rows RPW wave + RPI it .. of its stage.
+  // 64 lanes x 16 bytes from M0 + 1 KB it on, rows RPW wave + RPI it .. of its
+  // stage. Copy 0 of a stage buffer sets M0 (nothing else here uses it) and
+  // copies 1 .. NL - 1 follow it with no other copy in between.
   // The copies are issued from inline assembly: the compiler then neither
   // counts them nor orders LDS reads behind them (it cannot tell that they
   // write other stages than the ones being read), so every read of a stage
   // is preceded by an explicit wait_vmcnt and a workgroup barrier.
-  auto copy_one = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint32_t m0, int voff, int soff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "m0");
+  auto copy_one = [&](auto it_c, const __amdgpu_buffer_rsrc_t& rsrc, uint32_t m0, int voff, int soff) {
+    constexpr int IT = decltype(it_c)::value;
+    if constexpr (IT == 0) {
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+                   : "m0");
+    } else {
+      asm volatile("buffer_load_dwordx4 %0, %1, %2 offen offset:%3 lds"
+                   :
+                   : "v"(voff), "s"(rsrc), "s"(soff), "i"(IT * 1024));
+    }
   };
-  auto copy_k = [&](auto kb_c, int it, int row) {
+  auto copy_k = [&](auto kb_c, auto it_c, int row) {
     constexpr int KB = decltype(kb_c)::value;
-    copy_one(krsrc, lds_addr + (uint32_t)((KB * STAGE + (wave * RPW + it * RPI) * D) * 2),
-             kvoff[it], row * krow_b);
+    constexpr int IT = decltype(it_c)::value;
+    copy_one(it_c, krsrc, lds_addr + (uint32_t)((KB * STAGE + (wave * RPW) * D) * 2),
+             kvoff[IT], row * krow_b);
   };
-  auto copy_v = [&](auto vb_c, int it, int row) {
+  auto copy_v = [&](auto vb_c, auto it_c, int row) {
     constexpr int VB = decltype(vb_c)::value;
-    copy_one(vrsrc, lds_addr + (uint32_t)(((R + VB) * STAGE + (wave * RPW + it * RPI) * D) * 2),
-             vvoff[it], row * vrow_b);
+    constexpr int IT = decltype(it_c)::value;
+    copy_one(it_c, vrsrc, lds_addr + (uint32_t)(((R + VB) * STAGE + (wave * RPW) * D) * 2),
+             vvoff[IT], row * vrow_b);
+  };
+  // Copy `it` of an unrolled loop (a constant after unrolling) as a
+  // compile-time index.
+  auto copy_k_at = [&](auto kb_c, int it, int row) {
+    if constexpr (NL > 0) if (it == 0) copy_k(kb_c, std::integral_constant<int, 0>{}, row);
+    if constexpr (NL > 1) if (it == 1) copy_k(kb_c, std::integral_constant<int, 1 % NL>{}, row);
+    if constexpr (NL > 2) if (it == 2) copy_k(kb_c, std::integral_constant<int, 2 % NL>{}, row);
+    if constexpr (NL > 3) if (it == 3) copy_k(kb_c, std::integral_constant<int, 3 % NL>{}, row);
+  };
+  auto copy_v_at = [&](auto vb_c, int it, int row) {
+    if constexpr (NL > 0) if (it == 0) copy_v(vb_c, std::integral_constant<int, 0>{}, row);
+    if constexpr (NL > 1) if (it == 1) copy_v(vb_c, std::integral_constant<int, 1 % NL>{}, row);
+    if constexpr (NL > 2) if (it == 2) copy_v(vb_c, std::integral_constant<int, 2 % NL>{}, row);
+    if constexpr (NL > 3) if (it == 3) copy_v(vb_c, std::integral_constant<int, 3 % NL>{}, row);
   };
 
   f32x16 o[DT];
@@ -472,10 +506,10 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     auto pro_copies = [&](auto x_c) {
       constexpr int X = decltype(x_c)::value;
 #pragma unroll
-      for (int it = 0; it < NL; ++it) copy_k(std::integral_constant<int, X>{}, it, srow[X]);
+      for (int it = 0; it < NL; ++it) copy_k_at(std::integral_constant<int, X>{}, it, srow[X]);
       if constexpr (X + 1 < R) {
 #pragma unroll
-        for (int it = 0; it < NL; ++it) copy_v(std::integral_constant<int, X>{}, it, srow[X]);
+        for (int it = 0; it < NL; ++it) copy_v_at(std::integral_constant<int, X>{}, it, srow[X]);
       }
     };
     pro_copies(std::integral_constant<int, 0>{});
@@ -563,9 +597,9 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
       if (k % CEVERY == 0) {
         const int c = k / CEVERY;
         if (c < NL) {
-          copy_v(std::integral_constant<int, VNEW>{}, c, srow[R - 2]);
+          copy_v_at(std::integral_constant<int, VNEW>{}, c, srow[R - 2]);
         } else {
-          copy_k(std::integral_constant<int, KNEW>{}, c - NL, srow[R - 1]);
+          copy_k_at(std::integral_constant<int, KNEW>{}, c - NL, srow[R - 1]);
         }
       }
 #pragma unroll

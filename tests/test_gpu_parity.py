@@ -294,6 +294,48 @@ def test_strided_views_match_contiguous(d, bq, bk):
         assert torch.isnan(obuf[:, :, :2].float()).all()
 
 
+@pytest.mark.parametrize("d,row_stride", [(128, 0), (128, 8), (64, 0), (64, 8), (128, 40)])
+def test_small_and_zero_row_strides(d, row_stride):
+    """K and V views whose rows are closer together than head_dim (stride 8:
+    overlapping rows) or all the same row (stride 0), as the header's stride
+    rule allows: selection, sparse, dense and causal results are bitwise those
+    of the same values in contiguous tensors."""
+    case = synth.make_case(f"rowstride{d}_{row_stride}", hq=2, hkv=1, d=d, prefix=64, gen=448,
+                           cfg=70 + d + row_stride)
+    lay = case.layout
+    b, lk = lay["batch"], lay["kv_len"]
+    note(f"[gpu] K/V row stride {row_stride} elements, head_dim {d}, {lay}")
+    q, k0, v0 = case_to_gpu(case)
+    per = (lk - 1) * row_stride + d  # elements one batch entry's rows span
+    views = []
+    for src in (k0, v0):
+        base = torch.empty(b * per, dtype=torch.bfloat16, device=q.device)
+        flat = src.reshape(b, lk, d)
+        # row t of the view starts at t * row_stride; with overlapping rows the
+        # later rows overwrite the shared elements, so take the view's own values
+        for bi in range(b):
+            for t in range(lk):
+                base[bi * per + t * row_stride: bi * per + t * row_stride + d] = flat[bi, t]
+        views.append(torch.as_strided(base, (b, lk, 1, d), (per, row_stride, d, 1)))
+    ks, vs = views
+    kc, vc = ks.contiguous(), vs.contiguous()
+    keep = _keep(lay, 50)
+    idx, cnt = bsa.select_blocks(q, kc, lay, keep)
+    idx_s, cnt_s = bsa.select_blocks(q, ks, lay, keep)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_s) and torch.equal(cnt, cnt_s)
+    pairs = [
+        (bsa.block_sparse_attention(q, kc, vc, idx, cnt, lay),
+         bsa.block_sparse_attention(q, ks, vs, idx, cnt, lay)),
+        (bsa.dense_attention(q, kc, vc, lay), bsa.dense_attention(q, ks, vs, lay)),
+        (bsa.dense_attention(q, kc, vc, lay, causal=True),
+         bsa.dense_attention(q, ks, vs, lay, causal=True)),
+    ]
+    torch.cuda.synchronize()
+    for ref, got in pairs:
+        assert torch.equal(ref.view(torch.int16), got.view(torch.int16))
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_list_chunk_boundaries(d):
     """Block lists of 64, 65, 129 and 140 entries (the kernel reads a list 64
