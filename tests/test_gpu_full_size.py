@@ -4,8 +4,8 @@ attention kernel, both on torch's current stream).
 
 Selection is compared with the oracle for every (head, query block) bit for
 bit. Attention is compared with the oracle on every real row for the 48k
-edge-video workload, the dense 8k workload and the first sparse layer of the
-two-stream schedule (one query head per worker process), and on sampled
+edge-video workload, the dense 8k workload and the first dense and first
+sparse layers of the two-stream schedule (one query head per worker process), and on sampled
 query rows elsewhere (rows 0 and q_valid - 1 of
 every head plus uniform draws), which the oracle computes one by one; padded
 query rows must be exactly 0 everywhere.
@@ -200,8 +200,7 @@ def test_twostream_schedule_layer(layer):
         what = f"sparse layer {layer}"
         # the protected understanding-stream blocks are in every real row
         assert (ridx[..., :p] == np.arange(p)).all(axis=-1)[rcnt > 0].all()
-    if layer == 8:  # the first sparse layer: every real row
+    if layer in (0, 8):  # the first dense and the first sparse layer: every real row
         _check_every_row(case, out, lse, ridx, rcnt, what)
     else:
-        _check_rows(case, out, lse, ridx, rcnt, 256 if layer == 0 else 32, seed_layer=layer,
-                    what=what)
+        _check_rows(case, out, lse, ridx, rcnt, 32, seed_layer=layer, what=what)
