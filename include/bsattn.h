@@ -17,7 +17,8 @@
  *   framework allocator). The library allocates no memory on any call path.
  * - Every call is asynchronous on `stream` (0 = the null stream). No call
  *   synchronises the host, and none copies host memory to the device: all
- *   metadata travels as kernel arguments.
+ *   metadata travels as kernel arguments. (The list-checking build is the
+ *   exception: see attn_block_sparse_fwd.)
  * - q, k, v, out: bf16, 16-byte aligned, head_dim contiguous, element
  *   strides given per (batch, sequence, head) in `attn_shape`, each a
  *   multiple of 8.
