@@ -26,7 +26,9 @@
 // What the main loop issues per wave and 64-key stage is kept to what the
 // matrix products need: on gfx950 every vector, scalar and LDS instruction a
 // SIMD issues between its matrix instructions costs matrix-core time, and so
-// does every wait on memory.
+// does every wait on memory. Under this load the chip also runs at its power
+// limit, so every byte moved (stage copies through L2, LDS operand reads)
+// costs clock.
 //  * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: the K fragment (A operand)
 //    comes from LDS, Q^T (B operand) stays in registers for the whole
 //    kernel. Each lane owns one query row and half of the wave's 32 keys.
@@ -46,7 +48,8 @@
 //    of the next.
 //  * K and V stages move HBM -> LDS with buffer_load_dwordx4 ... lds (no
 //    VGPR staging): the buffer resource of the (batch, KV head) and each
-//    lane's offset are fixed, the stage enters as one scalar byte offset.
+//    lane's offset are fixed, the stage enters as one scalar byte offset,
+//    and M0 (the LDS destination) is set once per stage buffer.
 //    Rows are XOR-swizzled in 16-byte chunks so the K row reads and the V
 //    transpose reads hit distinct banks. K and V each have a ring of R
 //    stages in LDS and are copied R - 1 stages ahead of their use, so a
