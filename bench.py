@@ -16,8 +16,12 @@ selection time included in the denominator); the attention kernel alone is
 reported in ``roofline`` against the bf16 MFMA peak, timed with HIP events on
 the stream the kernels are launched on.
 
+After the timed region the step runs back to back for a few more seconds
+while the driver's energy counter is read (``power``: average socket power
+against the power cap, per-XCD shader clocks); these launches are not timed.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload edge48k]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--power-seconds S]
 """
 from __future__ import annotations
 
@@ -76,6 +80,10 @@ def parse():
     ap.add_argument("--input-sets", type=int, default=3,
                     help="distinct input sets rotated over the steps (twostream: always its 36 layers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power-seconds", type=float, default=4.0,
+                    help="after the timed region, run the step back to back for about this long "
+                         "and report average socket power and shader clocks from the driver's "
+                         "energy counter (0: skip)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="also run one plain device copy of BYTES bytes (a known-size kernel "
                          "for scaling hardware byte counters)")
@@ -230,6 +238,109 @@ class SclkSampler:
         self.done.set()
         self.thread.join(timeout=1.0)
         return max(self.seen) if len(self.seen) >= self.min_samples else None
+
+
+def power_from_readings(readings, cap_w=None):
+    """Average socket power over the driver's energy-counter windows.
+
+    `readings` are (timestamp_ns, energy_count, resolution_uJ, gfxclks_mhz)
+    tuples, one per counter update (the counter advances about once a
+    second), all taken while the step ran back to back. The average is the
+    energy between the first and the last update over the time between
+    them; the clocks are the per-XCD means over the updates after the first
+    (each update reports the clocks of the window it closes). None with
+    fewer than two updates."""
+    if len(readings) < 2:
+        return None
+    t0, e0, res, _ = readings[0]
+    t1, e1, _, _ = readings[-1]
+    if t1 <= t0:
+        return None
+    avg_w = (e1 - e0) * res * 1e-6 / ((t1 - t0) * 1e-9)
+    clks = [r[3] for r in readings[1:] if r[3]]
+    per_xcd = None
+    if clks and all(len(c) == len(clks[0]) for c in clks):
+        per_xcd = [round(float(np.mean([c[x] for c in clks])), 1) for x in range(len(clks[0]))]
+    windows = []
+    for (ta, ea, ra, _), (tb, eb, _, _) in zip(readings, readings[1:]):
+        if tb > ta:
+            windows.append((eb - ea) * ra * 1e-6 / ((tb - ta) * 1e-9))
+    return {
+        "avg_w": round(avg_w, 1),
+        "window_w_min": round(min(windows), 1),
+        "window_w_max": round(max(windows), 1),
+        "windows": len(readings) - 1,
+        "seconds": round((t1 - t0) * 1e-9, 3),
+        "cap_w": cap_w,
+        "gfxclk_mhz_per_xcd": per_xcd,
+        "gfxclk_mhz_mean": round(float(np.mean(per_xcd)), 1) if per_xcd else None,
+    }
+
+
+def measure_power(run_step, dev, seconds):
+    """Runs `run_step(i)` back to back for about `seconds` after the timed
+    region (at most two steps queued) and reads the driver's energy counter
+    and shader clocks through amdsmi at each counter update. Returns
+    power_from_readings() of those updates, or None where amdsmi is missing,
+    the device is not found or fewer than two updates fell inside."""
+    if seconds <= 0:
+        return None
+    try:
+        import amdsmi
+    except ImportError:
+        return None
+    import torch
+    try:
+        amdsmi.amdsmi_init()
+    except Exception:
+        return None
+    try:
+        prop = torch.cuda.get_device_properties(dev)
+        bdf = f"{prop.pci_domain_id:04x}:{prop.pci_bus_id:02x}:{prop.pci_device_id:02x}"
+        handle = None
+        for h in amdsmi.amdsmi_get_processor_handles():
+            if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(bdf):
+                handle = h
+        if handle is None:
+            return None
+        try:
+            cap_w = round(amdsmi.amdsmi_get_power_cap_info(handle)["power_cap"] / 1e6, 1)
+        except Exception:
+            cap_w = None
+        ring = [torch.cuda.Event() for _ in range(2)]
+        readings, last_ts = [], None
+        t_end = time.perf_counter() + seconds
+        next_poll = 0.0
+        i = 0
+        while time.perf_counter() < t_end:
+            if i >= len(ring):
+                ring[i % len(ring)].synchronize()
+            run_step(i)
+            ring[i % len(ring)].record()
+            i += 1
+            now = time.perf_counter()
+            if now < next_poll or i < len(ring):
+                continue
+            next_poll = now + 0.02
+            e = amdsmi.amdsmi_get_energy_count(handle)
+            if e["timestamp"] != last_ts:
+                last_ts = e["timestamp"]
+                try:
+                    clks = [int(c) for c in amdsmi.amdsmi_get_gpu_metrics_info(handle)
+                            .get("current_gfxclks", []) if str(c).isdigit() and int(c) < 0xFFFF]
+                except Exception:
+                    clks = []
+                readings.append((e["timestamp"], e["energy_accumulator"],
+                                 e["counter_resolution"], clks))
+        torch.cuda.synchronize()
+        # The first reading is the counter as the loop found it, the second
+        # closes a window that began before the loop: average from the second.
+        return power_from_readings(readings[1:], cap_w)
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
 
 def cpu_model():
@@ -521,6 +632,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sclk = clock.stop()
+    power = measure_power(step, dev, args.power_seconds)
     kinds = [kind for _, kind in plan[0]]
     main_calls = [j for j, kind in enumerate(kinds) if kind != "und"]
     und_calls = [j for j, kind in enumerate(kinds) if kind == "und"]
@@ -571,6 +683,8 @@ def main():
         "select_ms_per_step": round(float(np.mean(sel_ms)), 4),
         "selector": None,
         "gpu_sclk_mhz_max_seen": sclk,
+        # average socket power and shader clocks with the step running back to back
+        "power": power,
         # the bf16 MFMA peak scales with the shader clock (4096 FLOP per CU per cycle)
         "attn_frac_of_peak_at_seen_clock": (round(att_tflops / (256 * 4096 * sclk * 1e6 / 1e12), 4)
                                             if sclk else None),

@@ -1,0 +1,51 @@
+"""The benchmark's reduction of the driver's energy-counter readings to an
+average socket power (host logic only; the live readings need a GPU)."""
+import bench
+
+RES_UJ = 15.3  # counter resolution in microjoules, as the driver reports it
+
+
+def _counts(joules):
+    return round(joules / (RES_UJ * 1e-6))
+
+
+def test_constant_power_over_whole_windows():
+    # 1,390 W for three one-second windows, then 1,400 W for one
+    e = [0, _counts(1390), _counts(2780), _counts(4170), _counts(5570)]
+    ts = [10**9 * (5 + k) for k in range(5)]
+    clk = [[1650 + x for x in range(8)]] * 5
+    r = bench.power_from_readings(list(zip(ts, e, [RES_UJ] * 5, clk)), cap_w=1400.0)
+    assert abs(r["avg_w"] - 5570 / 4) < 0.5
+    assert abs(r["window_w_min"] - 1390) < 0.5 and abs(r["window_w_max"] - 1400) < 0.5
+    assert r["windows"] == 4 and abs(r["seconds"] - 4.0) < 1e-9
+    assert r["cap_w"] == 1400.0
+    assert r["gfxclk_mhz_per_xcd"] == [1650.0 + x for x in range(8)]
+    assert r["gfxclk_mhz_mean"] == 1653.5
+
+
+def test_uneven_windows_weigh_by_time():
+    # 0.5 s at 1,000 W then 1.5 s at 1,400 W: 1,300 W on average
+    ts = [0, 5 * 10**8, 2 * 10**9]
+    e = [0, _counts(500), _counts(500 + 2100)]
+    r = bench.power_from_readings([(t, x, RES_UJ, []) for t, x in zip(ts, e)])
+    assert abs(r["avg_w"] - 1300) < 0.5
+    assert r["gfxclk_mhz_per_xcd"] is None and r["gfxclk_mhz_mean"] is None
+
+
+def test_clocks_come_from_the_windows_inside_the_load():
+    # the first reading's clocks describe the window before the first update
+    ts = [0, 10**9, 2 * 10**9]
+    clk = [[100] * 8, [1600] * 8, [1700] * 8]
+    r = bench.power_from_readings([(t, _counts(1400) * k, RES_UJ, c)
+                                   for k, (t, c) in enumerate(zip(ts, clk))])
+    assert r["gfxclk_mhz_per_xcd"] == [1650.0] * 8
+
+
+def test_too_few_readings():
+    assert bench.power_from_readings([]) is None
+    assert bench.power_from_readings([(0, 0, RES_UJ, [])]) is None
+    assert bench.power_from_readings([(5, 0, RES_UJ, []), (5, 10, RES_UJ, [])]) is None
+
+
+def test_power_phase_off():
+    assert bench.measure_power(lambda i: None, None, 0) is None
