@@ -685,6 +685,10 @@ def main():
         "gpu_sclk_mhz_max_seen": sclk,
         # average socket power and shader clocks with the step running back to back
         "power": power,
+        # the bf16 MFMA peak at the mean shader clock of that phase
+        "attn_frac_of_peak_at_sustained_clock": (
+            round(att_tflops / (256 * 4096 * power["gfxclk_mhz_mean"] * 1e6 / 1e12), 4)
+            if power and power.get("gfxclk_mhz_mean") else None),
         # the bf16 MFMA peak scales with the shader clock (4096 FLOP per CU per cycle)
         "attn_frac_of_peak_at_seen_clock": (round(att_tflops / (256 * 4096 * sclk * 1e6 / 1e12), 4)
                                             if sclk else None),
