@@ -241,8 +241,20 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   // three 64-row workgroups, and the three cohorts of 32 start a third of
   // their lists apart. The order depends on blockIdx only, so results stay
   // bitwise reproducible.
+  // The half-lifetime lag builds up over the first rounds: both cohorts of
+  // round 0 start together, and the second cohort's lag grows to about half
+  // a lifetime by round 6 (measured on XCD 0 at 48k: 0, 13, 20, 23, 27, 29
+  // and 30 sixty-fourths of a lifetime in rounds 0-6). At head_dim 128 the
+  // second cohort of round r starts kLead64[min(r, 7)] sixty-fourths into
+  // its list: 0, 16, 24, 28, 30, 31, 32, 32, a little ahead of the lags,
+  // which timed best among the tables tried.
   const int cohort = (w >> 8) % (D == 64 ? 3 : 2);  // (w / 8) / 32: cohorts of 32 per XCD
-  const int n_first = (NQG == 2) ? (cohort * nblk) / (D == 64 ? 3 : 2) : 0;
+  int n_first = (NQG == 2) ? (cohort * nblk) / (D == 64 ? 3 : 2) : 0;
+  if constexpr (NQG == 2 && D == 128) {
+    constexpr uint64_t kLead64 = 0x8207de718400ull;  // 6 bits per round, round 0 lowest
+    const int rnd = min(kx >> 6, 7);                 // round of 64 workgroups on the XCD
+    n_first = cohort ? ((int)((kLead64 >> (6 * rnd)) & 63) * nblk) >> 6 : 0;
+  }
 
   // Block j as a descriptor: (first key row << 8) | real keys in the block,
   // 0 for an entry outside [0, NK) (copied from block 0, every key masked).
