@@ -381,3 +381,54 @@ def test_large_and_growing_logits(d):
     kf = synth.bf16_bits_to_f32(base.k).astype(np.float64) * ramp
     case = dataclasses.replace(base, q=synth.to_bf16_bits(qf), k=synth.to_bf16_bits(kf))
     _full_check(case, 60)
+
+
+@pytest.mark.parametrize("d,hkv", [(128, 8), (64, 32)])
+def test_every_dispatch_round(d, hkv):
+    """Enough 64-row workgroups (32 heads x 127 query blocks = 4,064, 508 per
+    XCD) that every XCD reaches its eighth round of 64 (head_dim 128, two
+    workgroups per CU; the eighth round starts the last entry of the start
+    table) or its sixth of 96 (head_dim 64, three per CU). Every list start the kernel derives from
+    the dispatch order is then used: each round's start of the second cohort
+    at head_dim 128, the thirds at head_dim 64, and the wrap-around to the
+    list's start. Selected-block and dense attention are compared with the
+    oracle on every real row (dense as every block listed); causal attention
+    on four heads."""
+    from full_oracle import check_every_row
+    case = synth.make_case("rounds", cfg=65, hq=32, hkv=hkv, d=d, bq=64, bk=64, prefix=100,
+                           gen=8100)
+    lay = case.layout
+    nq, nk, p = bsa.num_blocks(lay)
+    assert lay["batch"] * lay["num_q_heads"] * nq // 8 > 7 * 64
+    keep = bsa.keep_blocks(nk, p, 75)
+    q, k, v = case_to_gpu(case)
+    idx, cnt = bsa.select_blocks(q, k, lay, keep)
+    out, lse = bsa.block_sparse_attention(q, k, v, idx, cnt, lay, return_lse=True)
+    dense, dlse = bsa.dense_attention(q, k, v, lay, return_lse=True)
+    causal, clse = bsa.dense_attention(q, k, v, lay, causal=True, return_lse=True)
+    torch.cuda.synchronize()
+    ridx, rcnt = oracle.select(lay, case.q, case.k, keep)
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert np.array_equal(gc, rcnt) and np.array_equal(gi, ridx), "selection differs"
+    every = np.broadcast_to(np.arange(nk, dtype=np.int32), (lay["batch"], lay["num_q_heads"], nq, nk))
+    full = np.full((lay["batch"], lay["num_q_heads"], nq), nk, dtype=np.int32)
+    for name, got, gl, li, lc in (("sparse", out, lse, gi, gc), ("dense", dense, dlse, every, full)):
+        bits = got.view(torch.int16).cpu().numpy().view(np.uint16)
+        mx, mean, lse_err, pad_zero, lse_fin = check_every_row(case, np.ascontiguousarray(li), lc,
+                                                               bits, gl.cpu().numpy())
+        note(f"[gpu] rounds d={d} {name}: every real row max-abs {mx:.3g} mean-abs {mean:.3g} "
+             f"lse {lse_err:.3g}")
+        assert mx <= 2e-2 and mean <= 2e-3, f"{name}: max-abs {mx:.3g}, mean-abs {mean:.3g}"
+        assert pad_zero and lse_fin and lse_err < 1e-3, name
+    g = out_to_f64(causal)
+    gl = clse.cpu().numpy().astype(np.float64)
+    rows = _row_mask(lay)
+    grp = lay["num_q_heads"] // lay["num_kv_heads"]
+    lay1 = dict(lay, num_q_heads=1, num_kv_heads=1)
+    for h in (0, 9, 18, 31):
+        ro, rl = oracle.dense_causal(lay1, np.ascontiguousarray(case.q[:, :, h:h + 1]),
+                                     np.ascontiguousarray(case.k[:, :, h // grp:h // grp + 1]),
+                                     np.ascontiguousarray(case.v[:, :, h // grp:h // grp + 1]))
+        live = np.isfinite(rl[:, 0]) & rows
+        assert_close(g[:, :, h][live], ro[:, :, 0][live], what=f"causal head {h}")
+        assert np.abs(gl[:, h][live] - rl[:, 0][live]).max() < 1e-3
