@@ -142,6 +142,30 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
 template <int D, int NQG>
 constexpr int kv_ring() { return 2; }
 
+// Work split inside each XCD pair. Under the power limit the odd-numbered
+// XCDs run at a lower shader clock than the even ones (0.95-0.97 of it on
+// every box measured, in every workload that keeps the chip busy), so with
+// equal shares the even XCDs finish early and idle. A launch in which every
+// XCD runs at least 32 rounds of its resident workgroups gives the even XCD
+// of each pair 50.6 % of the pair's work (the best of the shares timed at
+// 48k; larger ones cost more in L2 locality than they save). A shorter
+// launch splits evenly: a larger share that adds a partial round costs more
+// than the clocks (8 rounds at dense 8k: 4.8 % slower). The split depends
+// only on the launch's shape, so results stay bitwise reproducible.
+constexpr int kEvenShare16 = 33161;  // 0.506 x 65536
+
+__host__ __device__ __forceinline__ int even_count(int pair_work, int share16) {
+  return (int)(((int64_t)pair_work * share16 + 32768) >> 16);
+}
+
+template <int D, int NQG>
+int pair_split(const AttnParams& p) {
+  constexpr int resident = NQG == 2 ? (D == 64 ? 3 : 2) : 1;  // workgroups per CU
+  const int per_xcd = (p.n_wg + 7) / 8;
+  const bool long_launch = per_xcd >= 32 * 32 * resident;  // 32 rounds on 32 CUs
+  return (D == 128 && !p.head_sync && long_launch) ? kEvenShare16 : 32768;
+}
+
 template <int D, int BK, int NQG, int MODE>
 __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __restrict__ smem) {
   constexpr bool DENSE = MODE != kSparse;    // the list is every non-empty block
@@ -192,8 +216,17 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
     lin = xcd * per + kx % per;
     if (lin >= tot) return;  // padding: the whole workgroup leaves before any barrier
   } else {
-    const int nwg = p.n_wg, per = nwg >> 3, rem = nwg & 7;
-    const int all = xcd * per + min(xcd, rem) + kx;
+    // The work goes to the four XCD pairs as evenly as possible, and within
+    // a pair the even XCD takes even_share16 / 65536 of it (pair_split).
+    // The grid gives every XCD as many workgroups as the largest share; an
+    // odd XCD's surplus ones have no work.
+    const int nwg = p.n_wg, q4 = nwg >> 2, r4 = nwg & 3;
+    const int j = xcd >> 1;
+    const int pj = q4 + (j < r4 ? 1 : 0);
+    const int ej = even_count(pj, p.even_share16);
+    const int start = j * q4 + min(j, r4) + ((xcd & 1) ? ej : 0);
+    if (kx >= ((xcd & 1) ? pj - ej : ej)) return;  // leaves before any barrier
+    const int all = start + kx;
     const int tot = p.nq * p.group * p.qparts;
     bg = all / tot;
     lin = all % tot;
@@ -771,10 +804,13 @@ attn_fwd_kernel(const AttnParams p) {
 
 template <int D, int BK, int NQG, int MODE>
 hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  const int grid =
-      p.head_sync ? p.batch * p.hkv * 8 * ((p.nq * p.group * p.qparts + 7) / 8) : p.n_wg;
+  AttnParams q = p;
+  q.even_share16 = pair_split<D, NQG>(p);
+  const int pj0 = (p.n_wg >> 2) + ((p.n_wg & 3) ? 1 : 0);  // the largest pair's work
+  const int grid = p.head_sync ? p.batch * p.hkv * 8 * ((p.nq * p.group * p.qparts + 7) / 8)
+                               : 8 * even_count(pj0, q.even_share16);
   hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, MODE>), dim3(grid), dim3(128 * NQG), 0, stream,
-                     p);
+                     q);
   return hipGetLastError();
 }
 

@@ -31,6 +31,7 @@ struct AttnParams {
   int32_t qparts;           // workgroups per query block: block_q / 128 above 128 rows, else 1
   int32_t n_wg;             // workgroups with work: batch * hq * nq * qparts
   int32_t head_sync;        // 1: all XCDs on one KV head at a time (grid padded per head)
+  int32_t even_share16;     // 65536 x the share of each XCD pair's work its even XCD takes
   float scale_log2;         // softmax scale * log2(e)
   // Bytes from the first K (V) element of a (batch, KV head) to one past its
   // last one: the range of the copies' buffer resource (below 2^31).
