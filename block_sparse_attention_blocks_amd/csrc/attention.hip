@@ -148,7 +148,8 @@ constexpr int kv_ring() { return 2; }
 // equal shares the even XCDs finish early and idle. A launch in which every
 // XCD runs at least 32 rounds of its resident workgroups gives the even XCD
 // of each pair 50.6 % of the pair's work (the best of the shares timed at
-// 48k; larger ones cost more in L2 locality than they save). A shorter
+// 48k; larger ones cost more in L2 locality than they save), in the
+// contiguous order and, per KV head, in the head-synchronous one. A shorter
 // launch splits evenly: a larger share that adds a partial round costs more
 // than the clocks (8 rounds at dense 8k: 4.8 % slower). The split depends
 // only on the launch's shape, so results stay bitwise reproducible.
@@ -163,7 +164,7 @@ int pair_split(const AttnParams& p) {
   constexpr int resident = NQG == 2 ? (D == 64 ? 3 : 2) : 1;  // workgroups per CU
   const int per_xcd = (p.n_wg + 7) / 8;
   const bool long_launch = per_xcd >= 32 * 32 * resident;  // 32 rounds on 32 CUs
-  return (D == 128 && !p.head_sync && long_launch) ? kEvenShare16 : 32768;
+  return (D == 128 && long_launch) ? kEvenShare16 : 32768;
 }
 
 template <int D, int BK, int NQG, int MODE>
@@ -209,12 +210,25 @@ __device__ __forceinline__ void attn_fwd_body(const AttnParams& p, uint16_t* __r
   const int w = blockIdx.x;
   const int xcd = w & 7, kx = w >> 3;
   int lin, bg;
-  if (p.head_sync) {
+  if (p.head_sync && p.even_share16 == 32768) {
     const int tot = p.nq * p.group * p.qparts;  // workgroups per (batch, KV head)
     const int per = (tot + 7) >> 3;
     bg = kx / per;
     lin = xcd * per + kx % per;
     if (lin >= tot) return;  // padding: the whole workgroup leaves before any barrier
+  } else if (p.head_sync) {
+    // The same, with each (batch, KV head)'s work split between the XCDs of
+    // a pair as in the contiguous order below.
+    const int tot = p.nq * p.group * p.qparts;
+    const int q4 = tot >> 2, r4 = tot & 3;
+    const int per = even_count(q4 + (r4 ? 1 : 0), p.even_share16);  // per head and XCD
+    const int j = xcd >> 1;
+    const int pj = q4 + (j < r4 ? 1 : 0);
+    const int ej = even_count(pj, p.even_share16);
+    bg = kx / per;
+    const int loc = kx % per;
+    if (loc >= ((xcd & 1) ? pj - ej : ej)) return;  // leaves before any barrier
+    lin = j * q4 + min(j, r4) + ((xcd & 1) ? ej : 0) + loc;
   } else {
     // The work goes to the four XCD pairs as evenly as possible, and within
     // a pair the even XCD takes even_share16 / 65536 of it (pair_split).
@@ -807,7 +821,11 @@ hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   AttnParams q = p;
   q.even_share16 = pair_split<D, NQG>(p);
   const int pj0 = (p.n_wg >> 2) + ((p.n_wg & 3) ? 1 : 0);  // the largest pair's work
-  const int grid = p.head_sync ? p.batch * p.hkv * 8 * ((p.nq * p.group * p.qparts + 7) / 8)
+  const int tot = p.nq * p.group * p.qparts;                 // per (batch, KV head)
+  const int per_head = q.even_share16 == 32768 ? (tot + 7) / 8
+                                               : even_count((tot >> 2) + ((tot & 3) ? 1 : 0),
+                                                            q.even_share16);
+  const int grid = p.head_sync ? p.batch * p.hkv * 8 * per_head
                                : 8 * even_count(pj0, q.even_share16);
   hipLaunchKernelGGL((attn_fwd_kernel<D, BK, NQG, MODE>), dim3(grid), dim3(128 * NQG), 0, stream,
                      q);
