@@ -282,7 +282,8 @@ def measure_power(run_step, dev, seconds):
     region (at most two steps queued) and reads the driver's energy counter
     and shader clocks through amdsmi at each counter update. Returns
     power_from_readings() of those updates, or None where amdsmi is missing,
-    the device is not found or fewer than two updates fell inside."""
+    the device is not found, an amdsmi call fails or fewer than two updates
+    fell inside. Errors of the step itself propagate."""
     if seconds <= 0:
         return None
     try:
@@ -298,9 +299,12 @@ def measure_power(run_step, dev, seconds):
         prop = torch.cuda.get_device_properties(dev)
         bdf = f"{prop.pci_domain_id:04x}:{prop.pci_bus_id:02x}:{prop.pci_device_id:02x}"
         handle = None
-        for h in amdsmi.amdsmi_get_processor_handles():
-            if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(bdf):
-                handle = h
+        try:
+            for h in amdsmi.amdsmi_get_processor_handles():
+                if amdsmi.amdsmi_get_gpu_device_bdf(h).lower().startswith(bdf):
+                    handle = h
+        except Exception:
+            return None
         if handle is None:
             return None
         try:
@@ -322,7 +326,11 @@ def measure_power(run_step, dev, seconds):
             if now < next_poll or i < len(ring):
                 continue
             next_poll = now + 0.02
-            e = amdsmi.amdsmi_get_energy_count(handle)
+            try:
+                e = amdsmi.amdsmi_get_energy_count(handle)
+            except Exception:
+                readings = []
+                break
             if e["timestamp"] != last_ts:
                 last_ts = e["timestamp"]
                 try:

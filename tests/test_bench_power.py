@@ -1,5 +1,6 @@
-"""The benchmark's reduction of the driver's energy-counter readings to an
-average socket power (host logic only; the live readings need a GPU)."""
+"""The benchmark's power phase on the host: the reduction of the driver's
+energy-counter readings to an average socket power, and the phase's loop
+against a stand-in for the amdsmi module and torch's device calls (no GPU)."""
 import bench
 
 RES_UJ = 15.3  # counter resolution in microjoules, as the driver reports it
@@ -49,3 +50,83 @@ def test_too_few_readings():
 
 def test_power_phase_off():
     assert bench.measure_power(lambda i: None, None, 0) is None
+
+
+class _FakeSmi:
+    """Stands in for the amdsmi module: one device whose energy counter
+    advances by `watts` joules per update, each call being one update one
+    second after the last."""
+
+    def __init__(self, watts=1400.0, fail_energy=False):
+        self.watts, self.fail_energy = watts, fail_energy
+        self.ts, self.count, self.shut = 10**12, 0, False
+
+    def amdsmi_init(self):
+        pass
+
+    def amdsmi_shut_down(self):
+        self.shut = True
+
+    def amdsmi_get_processor_handles(self):
+        return ["h0"]
+
+    def amdsmi_get_gpu_device_bdf(self, h):
+        return "0000:8b:00.0"
+
+    def amdsmi_get_power_cap_info(self, h):
+        return {"power_cap": 1_400_000_000}
+
+    def amdsmi_get_energy_count(self, h):
+        if self.fail_energy:
+            raise RuntimeError("no energy counter")
+        self.ts += 10**9
+        self.count += round(self.watts / (RES_UJ * 1e-6))
+        return {"energy_accumulator": self.count, "counter_resolution": RES_UJ,
+                "timestamp": self.ts}
+
+    def amdsmi_get_gpu_metrics_info(self, h):
+        return {"current_gfxclks": [1700, 1620] * 4}
+
+
+def _fake_torch_cuda(monkeypatch):
+    import torch
+
+    class Prop:
+        pci_domain_id, pci_bus_id, pci_device_id = 0, 0x8B, 0
+
+    class Event:
+        def record(self):
+            pass
+
+        def synchronize(self):
+            pass
+
+    monkeypatch.setattr(torch.cuda, "get_device_properties", lambda dev: Prop())
+    monkeypatch.setattr(torch.cuda, "Event", Event)
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+
+
+def test_power_phase_loop_with_a_fake_driver(monkeypatch):
+    import sys
+    smi = _FakeSmi(1400.0)
+    monkeypatch.setitem(sys.modules, "amdsmi", smi)
+    _fake_torch_cuda(monkeypatch)
+    steps = []
+    r = bench.measure_power(steps.append, None, 0.15)
+    assert steps and steps == list(range(len(steps)))  # the step ran back to back
+    assert r is not None and abs(r["avg_w"] - 1400.0) < 0.5 and r["windows"] >= 2
+    assert r["cap_w"] == 1400.0 and r["gfxclk_mhz_per_xcd"] == [1700.0, 1620.0] * 4
+    assert smi.shut
+
+
+def test_power_phase_gives_up_quietly_when_the_driver_fails(monkeypatch):
+    import sys
+    smi = _FakeSmi(fail_energy=True)
+    monkeypatch.setitem(sys.modules, "amdsmi", smi)
+    _fake_torch_cuda(monkeypatch)
+    assert bench.measure_power(lambda i: None, None, 0.1) is None
+    assert smi.shut
+    other = _FakeSmi()
+    other.amdsmi_get_gpu_device_bdf = lambda h: "0000:01:00.0"  # not this device
+    monkeypatch.setitem(sys.modules, "amdsmi", other)
+    assert bench.measure_power(lambda i: None, None, 0.1) is None
